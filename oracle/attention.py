@@ -1,0 +1,234 @@
+"""Exact softmax attention in fp64 -- oracle, TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
+leg may import this module.  It shares nothing with the HIP library.
+
+What is computed (the plain definition the tiled method reaches exactly):
+
+    S = scale * Q K^T                 (N x N per batch b and head h)
+    causal: S[i, j] = -inf for j > i  (top-left aligned, N_q = N_k)
+    m_i = max_j S[i, j];  E = exp(S - m);  l_i = sum_j E[i, j];  P = E / l
+    O = P V;   LSE_i = m_i + ln l_i
+
+FlashAttention (IO-Awareness paper, abstract on the citation-hub page) is an
+*exact* attention algorithm: tiling moves data between HBM and on-chip memory
+but does not change the result, so the oracle is the definition itself.  The
+log-sum-exp output and the backward by recomputation are not spelled out on the
+pages; LSE is the natural log of the softmax normaliser (scale included), and
+the gradients below are the derivative of <dO, O> (softmax Jacobian):
+
+    D_i = sum_c dO[i, c] O[i, c]
+    dV = P^T dO;  dP = dO V^T;  dS = P * (dP - D 1^T)
+    dQ = scale * dS K;  dK = scale * dS^T Q
+
+The online-softmax recurrence (``attention_fwd_online``) follows the running
+maximum / running normaliser description on the FlashAttention-4
+related-papers page (online-softmax snippet) and the rescaling of the output
+accumulator named in the FlashAttention-3 Appendix B fragment (exp2, row_sum
+and O rescaling).  It is written out here only so that tests can check that
+the recurrence reaches the materialising result; the GPU does not use it.
+
+All arrays are [B, H, N, d]; inputs of any float dtype are widened to fp64.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "attention_fwd",
+    "attention_bwd",
+    "attention_fwd_loops",
+    "attention_fwd_online",
+    "attention_fwd_rows",
+    "default_scale",
+]
+
+
+def default_scale(d: int) -> float:
+    """Softmax scale 1/sqrt(d), the standard scaled dot-product choice."""
+    return 1.0 / math.sqrt(d)
+
+
+def _as64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def _scores(qb: np.ndarray, k: np.ndarray, scale: float, row0: int,
+            causal: bool) -> np.ndarray:
+    """Scaled scores of query rows [row0, row0+len(qb)) against all keys."""
+    s = (qb @ k.T) * scale
+    if causal:
+        rows = np.arange(row0, row0 + qb.shape[0])[:, None]
+        cols = np.arange(k.shape[0])[None, :]
+        s = np.where(cols > rows, -np.inf, s)
+    return s
+
+
+def _softmax_rows(s: np.ndarray):
+    """Row softmax of a score block; returns (P, m, l)."""
+    m = s.max(axis=1)
+    e = np.exp(s - m[:, None])
+    l = e.sum(axis=1)
+    return e / l[:, None], m, l
+
+
+def attention_fwd(q, k, v, causal: bool = False, scale: float | None = None,
+                  row_block: int = 1024):
+    """Materialising forward.  Returns (O [B,H,N,d] fp64, LSE [B,H,N] fp64).
+
+    Scores are built ``row_block`` query rows at a time to bound memory; each
+    block holds the complete rows of S, so this is still the plain definition.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = default_scale(d)
+    o = np.empty_like(q)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, N, row_block):
+                r1 = min(N, r0 + row_block)
+                s = _scores(q[b, h, r0:r1], k[b, h], scale, r0, causal)
+                p, m, l = _softmax_rows(s)
+                o[b, h, r0:r1] = p @ v[b, h]
+                lse[b, h, r0:r1] = m + np.log(l)
+    return o, lse
+
+
+def attention_fwd_rows(q, k, v, rows, causal: bool = False,
+                       scale: float | None = None):
+    """Forward for selected query rows of one head: q,k,v are [N, d].
+
+    Used to check full-size outputs at sampled rows.  Returns (O [len(rows), d],
+    LSE [len(rows)]) in fp64.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    d = q.shape[1]
+    if scale is None:
+        scale = default_scale(d)
+    rows = np.asarray(rows, dtype=np.int64)
+    s = (q[rows] @ k.T) * scale
+    if causal:
+        cols = np.arange(k.shape[0])[None, :]
+        s = np.where(cols > rows[:, None], -np.inf, s)
+    p, m, l = _softmax_rows(s)
+    return p @ v, m + np.log(l)
+
+
+def attention_bwd(q, k, v, do, causal: bool = False,
+                  scale: float | None = None, row_block: int = 1024):
+    """Materialising backward.  Returns (dQ, dK, dV), each [B,H,N,d] fp64.
+
+    Recomputes P from the definition (not from any saved tiled state) and
+    applies the softmax-Jacobian formulas in the module docstring.
+    """
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = default_scale(d)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            kb, vb = k[b, h], v[b, h]
+            for r0 in range(0, N, row_block):
+                r1 = min(N, r0 + row_block)
+                qb, dob = q[b, h, r0:r1], do[b, h, r0:r1]
+                s = _scores(qb, kb, scale, r0, causal)
+                p, _, _ = _softmax_rows(s)
+                ob = p @ vb
+                dd = (dob * ob).sum(axis=1)
+                dv[b, h] += p.T @ dob
+                dp = dob @ vb.T
+                ds = p * (dp - dd[:, None])
+                dq[b, h, r0:r1] = scale * (ds @ kb)
+                dk[b, h] += scale * (ds.T @ qb)
+    return dq, dk, dv
+
+
+def attention_fwd_loops(q, k, v, causal: bool = False,
+                        scale: float | None = None):
+    """Scalar triple loop over (query, key, channel); for N <= 16 only.
+
+    Written with no vector operations so that a reader can check it against the
+    definition term by term.  Used to pin the vectorised ``attention_fwd``.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = default_scale(d)
+    o = np.zeros_like(q)
+    lse = np.zeros((B, H, N), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                scores = []
+                for j in range(N):
+                    if causal and j > i:
+                        continue
+                    dot = 0.0
+                    for c in range(d):
+                        dot += q[b, h, i, c] * k[b, h, j, c]
+                    scores.append((j, scale * dot))
+                mx = max(s for _, s in scores)
+                total = 0.0
+                for _, s in scores:
+                    total += math.exp(s - mx)
+                for j, s in scores:
+                    w = math.exp(s - mx) / total
+                    for c in range(d):
+                        o[b, h, i, c] += w * v[b, h, j, c]
+                lse[b, h, i] = mx + math.log(total)
+    return o, lse
+
+
+def attention_fwd_online(q, k, v, causal: bool = False,
+                         scale: float | None = None, key_tile: int = 64,
+                         base2: bool = False):
+    """The online-softmax recurrence over key tiles, in fp64.
+
+    Keeps, per query row, a running maximum m, a running normaliser l and an
+    unnormalised output accumulator A; each key tile raises m if needed,
+    rescales l and A by exp(m_old - m_new), and adds its own exponentials.
+    ``base2`` runs the same recurrence with exp2 on scores pre-multiplied by
+    log2(e) (the exp2 form named in the FlashAttention-3 Appendix B fragment);
+    LSE is then ln2 * m2 + ln l.  A tile whose visible scores are all -inf
+    leaves the state untouched, so no NaN can arise.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = default_scale(d)
+    mult = scale * (1.0 / math.log(2.0) if base2 else 1.0)
+    expf = np.exp2 if base2 else np.exp
+    o = np.empty_like(q)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    rows = np.arange(N)[:, None]
+    for b in range(B):
+        for h in range(H):
+            m = np.full(N, -np.inf)
+            l = np.zeros(N)
+            acc = np.zeros((N, d))
+            for j0 in range(0, N, key_tile):
+                j1 = min(N, j0 + key_tile)
+                s = (q[b, h] @ k[b, h, j0:j1].T) * mult
+                if causal:
+                    cols = np.arange(j0, j1)[None, :]
+                    s = np.where(cols > rows, -np.inf, s)
+                m_new = np.maximum(m, s.max(axis=1))
+                live = np.isfinite(m_new)
+                alpha = np.zeros(N)
+                alpha[live] = expf(m[live] - m_new[live])
+                p = np.zeros_like(s)
+                p[live] = expf(s[live] - m_new[live, None])
+                l = alpha * l + p.sum(axis=1)
+                acc = alpha[:, None] * acc + p @ v[b, h, j0:j1]
+                m = m_new
+            o[b, h] = acc / l[:, None]
+            lse[b, h] = (m * math.log(2.0) if base2 else m) + np.log(l)
+    return o, lse

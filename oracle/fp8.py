@@ -1,0 +1,193 @@
+"""FP8 pieces of the oracle -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
+leg may import this module.  It shares nothing with the HIP library.
+
+Follows the FlashAttention-3 review page (abstract and core claim): FP8
+attention uses *block quantization* (one scale per block rather than per
+tensor) and *incoherent processing* (Q and K multiplied by a random orthogonal
+matrix before quantization, which spreads outliers while leaving Q K^T
+unchanged; the reference list points to Hadamard-based incoherence).  The
+pages give no construction, so this module takes the plainest one:
+
+  * e4m3 is the OCP "E4M3FN" 8-bit format (1 sign, 4 exponent bits with bias
+    7, 3 mantissa bits, no infinities, NaN = S.1111.111, largest finite 448,
+    subnormals down to 2^-9).  Encoding rounds to nearest, ties to even, and
+    saturates finite values to +-448.
+  * The rotation is x' = H_d (s o x) with H_d the unnormalised Sylvester
+    Hadamard matrix (entries +-1, H H^T = d I) and s a seeded +-1 vector shared
+    by Q and K.  V is not rotated.  Because (H s q).(H s k) = d (q.k), the
+    factor d is removed exactly by folding 1/d into Q's stored scale.
+  * H_d x is computed in fp32 by the fast Walsh-Hadamard transform with the
+    half-width h taking the values 1, 2, 4, ..., d/2 in that order; at each
+    level the pair (x[i], x[i+h]) with i & h == 0 becomes
+    (x[i] + x[i+h], x[i] - x[i+h]).  Fixing the order makes the fp32 result
+    reproducible bit for bit.
+  * Block scale = amax(|block|) / 448 in fp32 (1.0 when amax is 0); a block
+    is 128 consecutive rows of one (b, h) with all d columns.  The code of an
+    element is RNE_sat(x' / scale), the division done in fp32.  The per-tensor
+    baseline uses one amax over the whole tensor and no rotation.
+  * The fp8 attention result is exact attention on the dequantised values
+    (code value times stored scale); the device additionally rounds the
+    probabilities to e4m3, which the tests bound separately.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .attention import attention_fwd
+
+__all__ = [
+    "E4M3_MAX",
+    "e4m3_decode",
+    "e4m3_encode",
+    "hadamard",
+    "fwht_f32",
+    "quantize_fp8",
+    "dequantize_fp8",
+    "attention_fwd_fp8",
+]
+
+E4M3_MAX = 448.0
+_BIAS = 7
+
+
+def _decode_table() -> np.ndarray:
+    """Value of every one of the 256 e4m3 codes, from the format definition."""
+    t = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        sign = -1.0 if code & 0x80 else 1.0
+        field = (code >> 3) & 0xF
+        mant = code & 0x7
+        if field == 0xF and mant == 0x7:
+            t[code] = np.nan
+        elif field == 0:
+            t[code] = sign * (mant / 8.0) * 2.0 ** (1 - _BIAS)
+        else:
+            t[code] = sign * (1.0 + mant / 8.0) * 2.0 ** (field - _BIAS)
+    return t
+
+
+_TABLE = _decode_table()
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """uint8 codes -> fp64 values."""
+    return _TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Round values to e4m3 (nearest, ties to even, saturating); uint8 codes.
+
+    The grid spacing is 2^(e-3) for a value with binary exponent e >= -6 and
+    2^-9 below that (subnormals share the spacing of the smallest binade).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    neg = np.signbit(x)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    nan = np.isnan(x)
+    a = np.where(nan, 0.0, a)
+    _, ex = np.frexp(a)                 # a = f * 2^ex, f in [0.5, 1)
+    e = np.maximum(ex - 1, 1 - _BIAS)   # binary exponent, clamped to the subnormal one
+    quantum = np.ldexp(1.0, e - 3)
+    n = np.round(a / quantum)           # numpy rounds halves to even
+    val = n * quantum                   # exact; may step up one binade
+    _, ex2 = np.frexp(val)
+    e2 = ex2 - 1
+    normal = val >= 2.0 ** (1 - _BIAS)
+    field = np.where(normal, e2 + _BIAS, 0)
+    mant = np.where(normal, val / np.ldexp(1.0, np.where(normal, e2, 0)) * 8 - 8,
+                    val / 2.0 ** (1 - _BIAS) * 8)
+    mant = np.rint(mant).astype(np.int64)
+    field = np.where(val == 0, 0, field).astype(np.int64)
+    code = (neg.astype(np.int64) << 7) | (field << 3) | mant
+    code = np.where(nan, 0x7F, code)
+    return code.astype(np.uint8)
+
+
+def hadamard(d: int) -> np.ndarray:
+    """Unnormalised Sylvester Hadamard matrix H_d (d a power of two), fp64.
+
+    Built by the doubling H_2n = [[H_n, H_n], [H_n, -H_n]] from H_1 = [1].
+    """
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    h = np.ones((1, 1), dtype=np.float64)
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def fwht_f32(x) -> np.ndarray:
+    """H_d x over the last axis in fp32, half-width 1, 2, ..., d/2 in order."""
+    y = np.array(x, dtype=np.float32, copy=True)
+    d = y.shape[-1]
+    lead = y.shape[:-1]
+    h = 1
+    while h < d:
+        z = y.reshape(*lead, d // (2 * h), 2, h)
+        a = z[..., 0, :].copy()
+        b = z[..., 1, :].copy()
+        z[..., 0, :] = a + b
+        z[..., 1, :] = a - b
+        y = z.reshape(*lead, d)
+        h *= 2
+    return y
+
+
+def quantize_fp8(x, signs=None, scale_mul: float = 1.0,
+                 per_tensor: bool = False, block: int = 128):
+    """Block (or per-tensor) e4m3 quantisation of a [B, H, N, d] tensor.
+
+    ``x`` holds the values the device reads (bf16/fp16 widened, exact in fp32).
+    ``signs`` (length d, +-1) turns on the rotation x' = H_d(s o x).
+    Returns (codes uint8 [B,H,N,d], scales float32 [B,H,ceil(N/block)]); the
+    stored scale is (amax/448) * scale_mul, both operations in fp32.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    if signs is not None:
+        x = fwht_f32(x * np.asarray(signs, dtype=np.float32))
+    B, H, N, d = x.shape
+    nblk = -(-N // block)
+    pad = nblk * block - N
+    xa = np.abs(x)
+    if per_tensor:
+        amax = np.full((B, H, nblk), xa.max() if xa.size else 0.0,
+                       dtype=np.float32)
+    else:
+        xp = np.pad(xa, ((0, 0), (0, 0), (0, pad), (0, 0)))
+        amax = xp.reshape(B, H, nblk, block * d).max(axis=-1).astype(np.float32)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX),
+                     np.float32(1.0)).astype(np.float32)
+    rows_scale = np.repeat(scale, block, axis=2)[:, :, :N, None]
+    codes = e4m3_encode((x / rows_scale).astype(np.float32))
+    stored = (scale * np.float32(scale_mul)).astype(np.float32)
+    return codes, stored
+
+
+def dequantize_fp8(codes, scales, block: int = 128) -> np.ndarray:
+    """Code values times their block's stored scale, in fp64."""
+    vals = e4m3_decode(codes)
+    N = vals.shape[2]
+    s = np.repeat(np.asarray(scales, dtype=np.float64), block, axis=2)[:, :, :N]
+    return vals * s[..., None]
+
+
+def attention_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale,
+                      causal: bool = False, scale: float | None = None,
+                      block: int = 128):
+    """Exact attention on the dequantised fp8 operands; (O, LSE) in fp64.
+
+    With rotated Q and K and 1/d folded into Q's scale, the dequantised scores
+    equal scale * q.k up to quantisation error, so ``scale`` is the ordinary
+    softmax scale (1/sqrt(d) by default).
+    """
+    q = dequantize_fp8(q8, q_scale, block)
+    k = dequantize_fp8(k8, k_scale, block)
+    v = dequantize_fp8(v8, v_scale, block)
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    return attention_fwd(q, k, v, causal=causal, scale=scale)
