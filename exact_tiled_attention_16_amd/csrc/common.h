@@ -1,0 +1,119 @@
+// Device-side building blocks shared by the attention kernels (gfx950 only).
+//
+// Matrix-core layout facts used throughout (v_mfma_f32_32x32x16_{bf16,f16}
+// and v_mfma_f32_32x32x64_f8f6f4, wave64):
+//   * operand A (M x K): lane l holds row l%32 and eight (fp8: thirty-two)
+//     K-consecutive elements; operand B (K x N): lane l holds column l%32 and
+//     the same K slots.  Lanes l and l+32 hold the two halves of K.  Any
+//     permutation of K applied identically to A and B leaves the product
+//     unchanged, which the kernels use to pick convenient key orders.
+//   * accumulator (32 x 32, 16 floats per lane): register r of lane l holds
+//     row 8*(r/4) + 4*(l/32) + r%4 and column l%32.
+//   * ds_read_b64_tr_b16: inside each 16-lane group, lane j receives, as its
+//     element e (0..3), element j%4 of the 8-byte chunk addressed by lane
+//     4*e + j/4 of the same group.  With 4 x 4 lanes addressing rows r0+e and
+//     column groups c0+4*(j/4) of a row-major tile, lane j gets the column
+//     c0 + j of four consecutive rows: a transposed 16-bit read.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- 16-bit types
+
+// Element-type traits: DT 0 = bf16, 1 = fp16.
+template <int DT> struct Elem;
+
+template <> struct Elem<0> {
+  typedef bf16x8_t v8;
+  static __device__ __forceinline__ f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // Two fp32 values -> packed pair, round to nearest even.
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+  }
+};
+
+template <> struct Elem<1> {
+  typedef f16x8_t v8;
+  static __device__ __forceinline__ f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+  }
+};
+
+// ---------------------------------------------------------------- cross-lane
+
+// Combine a per-lane value with the one held 32 lanes away (same query row in
+// the accumulator layout).  permlane32_swap(x, x) returns the low half of x in
+// both halves of the first result and the high half in both of the second.
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                            false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                            false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------- memory
+
+__device__ __forceinline__ u32x4_t ld_global16(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+__device__ __forceinline__ void st_lds16(FA_LDS void* p, u32x4_t v) {
+  *reinterpret_cast<FA_LDS u32x4_t*>(p) = v;
+}
+
+__device__ __forceinline__ u32x4_t ld_lds16(const FA_LDS void* p) {
+  return *reinterpret_cast<const FA_LDS u32x4_t*>(p);
+}
+
+__device__ __forceinline__ s16x4_t ld_lds_tr16(const FA_LDS void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<FA_LDS s16x4_t*>(const_cast<FA_LDS void*>(p)));
+}
+
+// ---------------------------------------------------------------- scheduling
+
+// MI355X dispatches consecutive workgroup ids round-robin over its 8 XCDs,
+// each with a private L2.  Remap so that a contiguous range of logical ids
+// (the query tiles of one head, which stream the same K/V) runs on one XCD.
+__device__ __forceinline__ int xcd_remap(int bid, int nwg) {
+  constexpr int kXcd = 8;
+  const int full = (nwg / kXcd) * kXcd;
+  if (bid >= full) return bid;
+  return (bid % kXcd) * (nwg / kXcd) + bid / kXcd;
+}
+
+}  // namespace fa

@@ -1,0 +1,117 @@
+// C ABI of libfa.so (declared in include/fa.h): argument validation and
+// dispatch to the kernel launchers.  Nothing here allocates, frees or
+// synchronises; every check happens before anything is enqueued.
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "kernels.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+bool valid_dims(int B, int H, int N) {
+  if (B <= 0 || H <= 0 || N <= 0) return false;
+  // Workgroup counts and per-(b,h) row indices are 32-bit inside the kernels.
+  const int64_t bh = (int64_t)B * H;
+  return bh <= 0x7fffffff && (int64_t)N <= 0x7fffffff / 2;
+}
+
+bool supported_d(int d) { return d == 64 || d == 128 || d == 256; }
+
+bool valid_scale(float s) { return isfinite(s) && s > 0.f; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_str(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID: return "invalid argument (null or misaligned pointer, bad size, dtype or scale)";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration (head dimension must be 64, 128 or 256)";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, int dtype, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o) return FA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_INVALID;
+  if (!aligned4(lse)) return FA_ERR_INVALID;
+  if (!valid_dims(B, H, N) || (dtype != FA_BF16 && dtype != FA_FP16)) return FA_ERR_INVALID;
+  if (!valid_scale(scale) || (causal != 0 && causal != 1)) return FA_ERR_INVALID;
+  if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+  fa::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.N = N;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return launch_status(
+      fa::launch_fwd(a, B, H, d, dtype, causal != 0, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+// Entry points whose kernels are not built yet: validated, then reported as
+// unsupported so that callers fail loudly rather than receive garbage.
+extern "C" {
+
+int fa_quant_fp8(const void* x, int dtype, void* x8, float* scales, const float* signs,
+                 float scale_mul, int per_tensor, int B, int H, int N, int d, void* stream) {
+  (void)stream;
+  if (!x || !x8 || !scales) return FA_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(x8) || !aligned4(scales) || !aligned4(signs))
+    return FA_ERR_INVALID;
+  if (!valid_scale(scale_mul)) return FA_ERR_INVALID;
+  if (!valid_dims(B, H, N) || (dtype != FA_BF16 && dtype != FA_FP16)) return FA_ERR_INVALID;
+  if (per_tensor != 0 && per_tensor != 1) return FA_ERR_INVALID;
+  if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+  return FA_ERR_UNSUPPORTED;
+}
+
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_scale,
+               const float* k_scale, const float* v_scale, void* o, float* lse, int B, int H,
+               int N, int d, float scale, int causal, void* stream) {
+  (void)stream;
+  if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !o) return FA_ERR_INVALID;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o)) return FA_ERR_INVALID;
+  if (!aligned4(q_scale) || !aligned4(k_scale) || !aligned4(v_scale) || !aligned4(lse))
+    return FA_ERR_INVALID;
+  if (!valid_dims(B, H, N) || !valid_scale(scale) || (causal != 0 && causal != 1))
+    return FA_ERR_INVALID;
+  if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+  return FA_ERR_UNSUPPORTED;
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
+  if (!valid_dims(B, H, N) || !supported_d(d)) return 0;
+  return (size_t)B * H * N * sizeof(float);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, float* dq, void* dk, void* dv, void* workspace, int B, int H,
+           int N, int d, int dtype, float scale, int causal, void* stream) {
+  (void)stream;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+    return FA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) ||
+      !aligned4(lse))
+    return FA_ERR_INVALID;
+  if (!valid_dims(B, H, N) || (dtype != FA_BF16 && dtype != FA_FP16)) return FA_ERR_INVALID;
+  if (!valid_scale(scale) || (causal != 0 && causal != 1)) return FA_ERR_INVALID;
+  if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+  return FA_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"
+

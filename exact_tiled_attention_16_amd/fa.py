@@ -1,0 +1,160 @@
+"""ctypes binding of libfa.so with the C ABI's entry-point names.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind ``include/fa.h``.  torch provides device memory (tensors) and
+the stream (``torch.cuda.current_stream()``); there is no CPU or torch
+fallback -- a missing library raises ``OSError``.
+
+Raw entry points (``fa_fwd`` ...) take integers for pointers and streams and
+return the status code; the tensor helpers (``fwd`` ...) allocate outputs with
+torch, check shapes and raise ``FaError`` on a negative status.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_OK = 0
+FA_ERR_INVALID = -1
+FA_ERR_UNSUPPORTED = -2
+FA_ERR_LAUNCH = -3
+FA_BF16 = 0
+FA_FP16 = 1
+FP8_BLOCK = 128
+
+# Every symbol include/fa.h declares, with (restype, argtypes).
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+SIGNATURES = {
+    "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_quant_fp8": (_I, [_P, _I, _P, _P, _P, _F, _I, _I, _I, _I, _I, _P]),
+    "fa_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F,
+                        _I, _P]),
+    "fa_bwd_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                    _I, _F, _I, _P]),
+    "fa_status_str": (ctypes.c_char_p, [_I]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so once; raise if it is missing (build it first)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise OSError(f"{LIB_PATH} is missing; run "
+                          "`python -m exact_tiled_attention_16_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib
+
+
+class FaError(RuntimeError):
+    def __init__(self, code: int):
+        super().__init__(f"{status_str(code)} (status {code})")
+        self.code = code
+
+
+def status_str(code: int) -> str:
+    return lib().fa_status_str(int(code)).decode()
+
+
+def _check(code: int) -> None:
+    if code != FA_OK:
+        raise FaError(code)
+
+
+# ------------------------------------------------------------ raw entry points
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, dtype, scale, causal, stream) -> int:
+    return lib().fa_fwd(q, k, v, o, lse, B, H, N, d, dtype, scale, causal,
+                        stream)
+
+
+def fa_quant_fp8(x, dtype, x8, scales, signs, scale_mul, per_tensor, B, H, N,
+                 d, stream) -> int:
+    return lib().fa_quant_fp8(x, dtype, x8, scales, signs, scale_mul,
+                              per_tensor, B, H, N, d, stream)
+
+
+def fa_fwd_fp8(q8, k8, v8, qs, ks, vs, o, lse, B, H, N, d, scale, causal,
+               stream) -> int:
+    return lib().fa_fwd_fp8(q8, k8, v8, qs, ks, vs, o, lse, B, H, N, d,
+                            scale, causal, stream)
+
+
+def fa_bwd_workspace_size(B, H, N, d) -> int:
+    return lib().fa_bwd_workspace_size(B, H, N, d)
+
+
+def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, B, H, N, d, dtype, scale,
+           causal, stream) -> int:
+    return lib().fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, B, H, N, d,
+                        dtype, scale, causal, stream)
+
+
+# ------------------------------------------------------------ tensor helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float16:
+        return FA_FP16
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float16")
+
+
+def _check_tensor(t, name, shape=None, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _stream(t) -> int:
+    return _torch().cuda.current_stream(t.device).cuda_stream
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None,
+        out=None, lse=None):
+    """O, LSE = attention(q, k, v) for [B, H, N, d] bf16/fp16 device tensors."""
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(t, name, (B, H, N, d), q.dtype)
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor(out, "out", (B, H, N, d), q.dtype)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_tensor(lse, "lse", (B, H, N), torch.float32)
+    _check(fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                  lse.data_ptr(), B, H, N, d, dt, float(scale), int(bool(causal)),
+                  _stream(q)))
+    return out, lse

@@ -1,0 +1,152 @@
+/*
+ * fa.h -- C ABI of libfa.so: exact tiled softmax attention on AMD MI355X
+ * (gfx950).
+ *
+ * What is computed.  For every batch b and head h, with S = scale * Q K^T
+ * (N x N) and, when causal, S[i][j] = -inf for key j > query i (top-left
+ * alignment, equal query and key lengths):
+ *
+ *     O   = softmax_rows(S) V
+ *     LSE = m + ln(sum_j exp(S[i][j] - m)),   m = max_j S[i][j]   (natural log)
+ *
+ * This is exact attention ("FlashAttention: Fast and Memory-Efficient Exact
+ * Attention with IO-Awareness", abstract): the kernels stream key/value tiles
+ * through on-chip memory with an online softmax (running row maximum and
+ * normaliser, rescaled output accumulator; FlashAttention-4 related-papers
+ * page, online-softmax snippet) so the N x N matrix never reaches HBM, but
+ * the result is the definition above up to floating-point rounding.
+ *
+ * Layout.  Q, K, V, O, dO, dK, dV and the fp8 tensors are contiguous
+ * row-major [B][H][N][d] (d fastest).  LSE, the backward's D = rowsum(dO o O)
+ * and the fp8 block scales are contiguous [B][H][N] / [B][H][ceil(N/128)].
+ * Base pointers must be 16-byte aligned.  Offsets are 64-bit inside the
+ * library, so any tensor that fits in device memory is addressable.
+ *
+ * Ownership.  Every pointer is device memory owned by the caller.  The
+ * library allocates nothing, frees nothing and never synchronises; work is
+ * enqueued on the caller's stream (a hipStream_t passed as void*, NULL = the
+ * null stream) and completes asynchronously.  Inputs are read only; outputs
+ * are fully overwritten.  No global mutable state: calls are reentrant and may
+ * run concurrently on different streams as long as their output buffers do
+ * not overlap.
+ *
+ * Errors.  Argument problems are reported synchronously, before anything is
+ * enqueued: FA_ERR_INVALID for null pointers, non-positive sizes, unknown
+ * dtype, misaligned pointers or a non-finite or non-positive scale;
+ * FA_ERR_UNSUPPORTED for a head dimension other than 64, 128 or 256.
+ * FA_ERR_LAUNCH means the HIP runtime refused a kernel launch.  Faults inside
+ * a kernel surface at the caller's next synchronisation.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define FA_OK 0
+#define FA_ERR_INVALID (-1)
+#define FA_ERR_UNSUPPORTED (-2)
+#define FA_ERR_LAUNCH (-3)
+
+/* Element types of the 16-bit inputs. */
+#define FA_BF16 0
+#define FA_FP16 1
+
+/* Rows per fp8 quantisation block (per (b, h), all d columns). */
+#define FA_FP8_BLOCK 128
+
+/*
+ * fa_fwd -- attention forward.
+ *   q, k, v : [B][H][N][d] of `dtype` (FA_BF16 or FA_FP16), read only.
+ *   o       : [B][H][N][d] of `dtype`, written (rounded to nearest even).
+ *   lse     : [B][H][N] float, written; natural-log log-sum-exp of each
+ *             query row's scaled scores (scale included).  May be NULL when
+ *             the caller does not need it.
+ *   B, H, N : >= 1.  d : 64, 128 or 256.
+ *   scale   : softmax scale (1/sqrt(d) is the usual choice), finite, > 0.
+ *   causal  : 0 = full attention, 1 = key j visible to query i iff j <= i.
+ *   stream  : hipStream_t.
+ * The scores, probabilities and accumulators are fp32 inside the kernel;
+ * both products run on bf16/fp16 matrix-core instructions.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, int dtype, float scale, int causal,
+           void* stream);
+
+/*
+ * fa_quant_fp8 -- e4m3 quantisation for the fp8 forward
+ * ("FlashAttention-3: Fast and Accurate Attention with Asynchrony and
+ * Low-precision", abstract: block quantisation and incoherent processing).
+ *   x         : [B][H][N][d] of `dtype`, read only.
+ *   x8        : [B][H][N][d] uint8 e4m3 codes (OCP E4M3FN: bias 7, max 448,
+ *               no infinities), written.
+ *   scales    : [B][H][ceil(N/128)] float, written.  Dequantised element =
+ *               code value * scales[b][h][row/128].
+ *   signs     : device array of d floats, each +1 or -1, or NULL.  Non-NULL
+ *               applies the incoherent-processing rotation x' = H_d (s o x)
+ *               with H_d the unnormalised Sylvester Hadamard matrix,
+ *               computed in fp32 by the fast Walsh-Hadamard transform
+ *               (half-widths 1, 2, ..., d/2 in that order).  NULL = x' = x.
+ *   scale_mul : multiplies every stored scale (1/d for a rotated Q, so that
+ *               dequantised Q.K equals the unrotated product; else 1).
+ *   per_tensor: 0 = one scale per 128-row block of each (b, h);
+ *               1 = one scale for the whole tensor, written to every slot.
+ *   Scale = amax(|x'|) / 448 in fp32 (1 if the amax is 0), times scale_mul;
+ *   code = round-to-nearest-even of x' / (amax/448) in fp32, saturated to
+ *   +-448.  Per-tensor mode enqueues three kernels (block amax, reduction
+ *   into every slot of `scales`, quantisation); block mode enqueues one.
+ */
+int fa_quant_fp8(const void* x, int dtype, void* x8, float* scales,
+                 const float* signs, float scale_mul, int per_tensor,
+                 int B, int H, int N, int d, void* stream);
+
+/*
+ * fa_fwd_fp8 -- attention forward on e4m3 operands.
+ *   q8, k8, v8        : [B][H][N][d] e4m3 codes from fa_quant_fp8 (Q and K
+ *                       rotated with the same signs, Q with scale_mul 1/d).
+ *   q_scale, k_scale,
+ *   v_scale           : [B][H][ceil(N/128)] float block scales.
+ *   o                 : [B][H][N][d] bf16, written.
+ *   lse               : [B][H][N] float or NULL, as in fa_fwd.
+ *   scale, causal     : as in fa_fwd (the ordinary softmax scale).
+ * S = Q8 K8^T runs on fp8 matrix-core instructions with fp32 accumulation;
+ * block scales are folded into the fp32 scores and into the output
+ * rescaling; the probabilities are rounded to e4m3 for the second product
+ * while the row normaliser is summed from the fp32 values.
+ */
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
+               const float* q_scale, const float* k_scale,
+               const float* v_scale, void* o, float* lse, int B, int H, int N,
+               int d, float scale, int causal, void* stream);
+
+/*
+ * fa_bwd -- attention backward by recomputation.
+ *   q, k, v, o, dout : [B][H][N][d] of `dtype`, read only; o is the forward
+ *                      output and lse the forward's log-sum-exp [B][H][N].
+ *   dq               : [B][H][N][d] float, written (fp32 accumulation).
+ *   dk, dv           : [B][H][N][d] of `dtype`, written.
+ *   workspace        : device memory of at least
+ *                      fa_bwd_workspace_size(B, H, N, d) bytes; its contents
+ *                      on entry are ignored and on exit unspecified.
+ * Gradients of <dO, O>: with P the probabilities rebuilt from Q, K and LSE,
+ * D = rowsum(dO o O), dS = P o (dO V^T - D), the outputs are dV = P^T dO,
+ * dK = scale dS^T Q and dQ = scale dS K.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const void* dout, const float* lse, float* dq, void* dk, void* dv,
+           void* workspace, int B, int H, int N, int d, int dtype, float scale,
+           int causal, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* fa_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,126 @@
+"""C-ABI boundary checks that need no GPU.
+
+* libfa.so loads and exports every function include/fa.h declares;
+* the binding's names and argument counts match the header;
+* invalid arguments are rejected synchronously with the documented status
+  codes (no pointer is dereferenced and nothing is enqueued on these paths,
+  so the fake non-null addresses below are never touched).
+"""
+
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+# A 16-byte-aligned address that is never dereferenced on the error paths.
+FAKE = 0x10000
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    decls = {}
+    for m in re.finditer(r"\b(?:int|size_t|const char\*)\s+(fa_\w+)\s*\(([^)]*)\)\s*;",
+                         text):
+        args = [a for a in m.group(2).split(",") if a.strip() and a.strip() != "void"]
+        decls[m.group(1)] = len(args)
+    return decls
+
+
+@pytest.fixture(scope="module")
+def fa():
+    from exact_tiled_attention_16_amd import fa as mod
+    if not os.path.exists(mod.LIB_PATH):
+        pytest.fail("libfa.so is not built; run `python -m exact_tiled_attention_16_amd.build`")
+    mod.lib()
+    return mod
+
+
+def test_header_declares_expected_entry_points():
+    d = _declared()
+    assert {"fa_fwd", "fa_quant_fp8", "fa_fwd_fp8", "fa_bwd",
+            "fa_bwd_workspace_size", "fa_status_str"} <= set(d)
+
+
+def test_library_exports_every_declared_symbol(fa):
+    lib = fa.lib()
+    for name, nargs in _declared().items():
+        assert hasattr(lib, name), name
+        assert name in fa.SIGNATURES, name
+        assert len(fa.SIGNATURES[name][1]) == nargs, name
+
+
+def test_status_strings(fa):
+    for code in (fa.FA_OK, fa.FA_ERR_INVALID, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_LAUNCH):
+        assert fa.status_str(code) and fa.status_str(code) != "unknown status"
+    assert fa.status_str(12345) == "unknown status"
+
+
+def _fwd(fa, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=16, d=64,
+                dtype=fa.FA_BF16, scale=0.125, causal=0, stream=None)
+    args.update(kw)
+    return fa.fa_fwd(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1),
+    (dict(q=FAKE + 8), -1), (dict(o=FAKE + 2), -1), (dict(lse=FAKE + 2), -1),
+    (dict(B=0), -1), (dict(H=-1), -1), (dict(N=0), -1),
+    (dict(dtype=2), -1), (dict(scale=0.0), -1), (dict(scale=float("inf")), -1),
+    (dict(scale=float("nan")), -1), (dict(scale=-1.0), -1), (dict(causal=2), -1),
+    (dict(d=32), -2), (dict(d=96), -2), (dict(d=512), -2),
+])
+def test_fwd_rejects(fa, kw, code):
+    assert _fwd(fa, **kw) == code
+
+
+def test_quant_fp8_rejects(fa):
+    base = dict(x=FAKE, dtype=0, x8=FAKE, scales=FAKE, signs=None, scale_mul=1.0,
+                per_tensor=0, B=1, H=1, N=16, d=128, stream=None)
+    for kw, code in ((dict(x=None), -1), (dict(x8=None), -1), (dict(scales=None), -1),
+                     (dict(N=0), -1), (dict(dtype=5), -1), (dict(per_tensor=3), -1),
+                     (dict(d=100), -2), (dict(x=FAKE + 4), -1), (dict(x8=FAKE + 8), -1),
+                     (dict(scale_mul=0.0), -1), (dict(scales=FAKE + 2), -1)):
+        a = dict(base)
+        a.update(kw)
+        assert fa.fa_quant_fp8(**a) == code, kw
+
+
+def test_fwd_fp8_rejects(fa):
+    base = dict(q8=FAKE, k8=FAKE, v8=FAKE, qs=FAKE, ks=FAKE, vs=FAKE, o=FAKE, lse=None,
+                B=1, H=1, N=16, d=128, scale=0.1, causal=0, stream=None)
+    for kw, code in ((dict(q8=None), -1), (dict(vs=None), -1), (dict(o=None), -1),
+                     (dict(H=0), -1), (dict(scale=0.0), -1), (dict(causal=-1), -1),
+                     (dict(d=48), -2), (dict(k8=FAKE + 1), -1), (dict(o=FAKE + 8), -1)):
+        a = dict(base)
+        a.update(kw)
+        assert fa.fa_fwd_fp8(**a) == code, kw
+
+
+def test_bwd_rejects_and_workspace(fa):
+    assert fa.fa_bwd_workspace_size(4, 16, 4096, 128) >= 4 * 16 * 4096 * 4
+    assert fa.fa_bwd_workspace_size(0, 16, 4096, 128) == 0
+    assert fa.fa_bwd_workspace_size(1, 1, 16, 80) == 0
+    base = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE,
+                dv=FAKE, ws=FAKE, B=1, H=1, N=16, d=128, dtype=0, scale=0.1, causal=1,
+                stream=None)
+    for kw, code in ((dict(do=None), -1), (dict(lse=None), -1), (dict(ws=None), -1),
+                     (dict(dq=None), -1), (dict(N=-5), -1), (dict(dtype=7), -1),
+                     (dict(scale=float("nan")), -1), (dict(d=16), -2),
+                     (dict(dk=FAKE + 2), -1), (dict(dq=FAKE + 4), -1)):
+        a = dict(base)
+        a.update(kw)
+        assert fa.fa_bwd(**a) == code, kw
+
+
+def test_python_helpers_reject_bad_tensors(fa):
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fwd(q, q, q)  # host tensors are refused before any call
+    with pytest.raises(ValueError):
+        fa.fwd(torch.zeros(8, 64, dtype=torch.bfloat16), q, q)
