@@ -1,0 +1,321 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact tiled attention hot path on one MI355X.
+
+One *step* is one pass of the whole path over one synthetic batch of the
+bf16 forward-sweep workload at its longest sequence (B=2, H=16, N=8192,
+d=128; i.i.d. N(0,1) inputs, resident in HBM before timing starts):
+
+  fwd_bf16   fa_fwd, non-causal                        4*B*H*N^2*d flop
+  quant_fp8  fa_quant_fp8 on Q, K (rotated) and V        (no attention flop)
+  fwd_fp8    fa_fwd_fp8, non-causal                    4*B*H*N^2*d flop
+  bwd_bf16   fa_bwd, non-causal                    2.5*4*B*H*N^2*d flop
+
+Legs whose entry point is not built yet report FA_ERR_UNSUPPORTED at start-up
+and are left out of the step (listed under "legs_missing").  ``value`` is the
+step's attention flop divided by its wall time (HIP events on the launch
+stream around exactly --steps steps); per-leg figures and the roofline of the
+dominant kernel (average launch duration from per-launch events) are printed
+in the same JSON line, next to the fp64 oracle timed on a bounded sample on
+the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd TFLOP/s (bf16, fp8) at N=2k-16k, d=128; % of MFMA peak"
+# MI355X dense matrix-core peaks (256 CUs x 2.4 GHz): bf16/fp16 4096 and fp8
+# 8192 flop/clk/CU.
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}
+HBM_GBPS = 8000.0
+WORKLOAD = dict(B=2, H=16, N=8192, d=128)
+WORKLOAD_ID = 2  # the bf16 forward sweep's seeds
+
+# Kernel sources whose change invalidates stored traffic counters.
+KERNEL_SOURCES = {
+    "fwd_bf16": ["exact_tiled_attention_16_amd/csrc/fwd.hip",
+                 "exact_tiled_attention_16_amd/csrc/common.h"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def fwd_flops(B, H, N, d, causal=False):
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(leg):
+    """HBM bytes per launch from the committed counter summary, or None when
+    absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(leg)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != source_hash(KERNEL_SOURCES[leg]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def build_legs(torch, fa, dev):
+    from exact_tiled_attention_16_amd import inputs
+    B, H, N, d = (WORKLOAD[k] for k in "BHNd")
+    q, k, v = inputs.qkv(B, H, N, d, WORKLOAD_ID)
+    qd, kd, vd = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (q, k, v))
+    del q, k, v
+    scale = 1.0 / math.sqrt(d)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    legs = []
+
+    def fwd_call():
+        return fa.fa_fwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(),
+                         lse.data_ptr(), B, H, N, d, fa.FA_BF16, scale, 0, stream)
+    legs.append(dict(name="fwd_bf16", call=fwd_call, flops=fwd_flops(B, H, N, d),
+                     dtype="bf16", kernel="fwd_kernel"))
+
+    # fp8 quantisation + forward.
+    nblk = -(-N // fa.FP8_BLOCK)
+    signs = torch.from_numpy(inputs.signs(d, WORKLOAD_ID)).to(dev)
+    q8, k8, v8 = (torch.empty((B, H, N, d), dtype=torch.uint8, device=dev) for _ in range(3))
+    qs, ks, vs = (torch.empty((B, H, nblk), dtype=torch.float32, device=dev) for _ in range(3))
+    o8 = torch.empty_like(qd)
+    lse8 = torch.empty_like(lse)
+
+    def quant_call():
+        for x, x8, sc, sg, mul in ((qd, q8, qs, signs, 1.0 / d), (kd, k8, ks, signs, 1.0),
+                                   (vd, v8, vs, None, 1.0)):
+            rc = fa.fa_quant_fp8(x.data_ptr(), fa.FA_BF16, x8.data_ptr(), sc.data_ptr(),
+                                 sg.data_ptr() if sg is not None else None, mul, 0,
+                                 B, H, N, d, stream)
+            if rc != fa.FA_OK:
+                return rc
+        return fa.FA_OK
+
+    def fwd8_call():
+        return fa.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), qs.data_ptr(),
+                             ks.data_ptr(), vs.data_ptr(), o8.data_ptr(), lse8.data_ptr(),
+                             B, H, N, d, scale, 0, stream)
+    legs.append(dict(name="quant_fp8", call=quant_call, flops=0.0, dtype="fp8",
+                     kernel="quant_fp8_kernel"))
+    legs.append(dict(name="fwd_fp8", call=fwd8_call, flops=fwd_flops(B, H, N, d),
+                     dtype="fp8", kernel="fwd_fp8_kernel"))
+
+    # Backward on the same batch.
+    do = torch.from_numpy(inputs.dout(B, H, N, d, WORKLOAD_ID)).to(torch.bfloat16).to(dev)
+    dq = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    dk, dv = torch.empty_like(qd), torch.empty_like(qd)
+    wsz = fa.fa_bwd_workspace_size(B, H, N, d)
+    ws = torch.empty((max(wsz, 16),), dtype=torch.uint8, device=dev)
+
+    def bwd_call():
+        return fa.fa_bwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(),
+                         do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                         dv.data_ptr(), ws.data_ptr(), B, H, N, d, fa.FA_BF16, scale, 0,
+                         stream)
+    legs.append(dict(name="bwd_bf16", call=bwd_call, flops=2.5 * fwd_flops(B, H, N, d),
+                     dtype="bf16", kernel="bwd_kernel"))
+    return legs
+
+
+def cpu_baseline(legs_present, budget_s=15.0):
+    """Time the fp64 oracle on the host on a bounded sample of the same
+    workload: the first heads of batch 0, one at a time, until ~budget_s."""
+    import numpy as np
+    from exact_tiled_attention_16_amd import inputs
+    from oracle import attention as oatt
+    from oracle import fp8 as ofp8
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    B, H, N, d = (WORKLOAD[k] for k in "BHNd")
+    q, k, v = inputs.qkv(1, H, N, d, WORKLOAD_ID)
+    do = inputs.dout(1, H, N, d, WORKLOAD_ID)
+    s = inputs.signs(d, WORKLOAD_ID)
+    flops = 0.0
+    heads = 0
+    t0 = time.perf_counter()
+    while heads < H and time.perf_counter() - t0 < budget_s:
+        sl = (slice(0, 1), slice(heads, heads + 1))
+        qh, kh, vh, doh = q[sl], k[sl], v[sl], do[sl]
+        if "fwd_bf16" in legs_present:
+            oatt.attention_fwd(qh, kh, vh)
+            flops += fwd_flops(1, 1, N, d)
+        if "fwd_fp8" in legs_present:
+            q8, qs = ofp8.quantize_fp8(qh, signs=s, scale_mul=1.0 / d)
+            k8, ks = ofp8.quantize_fp8(kh, signs=s)
+            v8, vs = ofp8.quantize_fp8(vh)
+            ofp8.attention_fwd_fp8(q8, k8, v8, qs, ks, vs)
+            flops += fwd_flops(1, 1, N, d)
+        if "bwd_bf16" in legs_present:
+            oatt.attention_bwd(qh, kh, vh, doh)
+            flops += 2.5 * fwd_flops(1, 1, N, d)
+        heads += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle, legs {sorted(legs_present)}, {heads} of "
+                      f"{B * H} heads (b=0, h<{heads}) of B={B},H={H},N={N},d={d}, "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, run one device copy of this many MiB "
+                         "(reference kernel for the traffic counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(each (batch, head) shard would run the same kernel with no "
+              "communication). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from exact_tiled_attention_16_amd import fa
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fa.lib()
+    legs_all = build_legs(torch, fa, dev)
+    torch.cuda.synchronize()
+
+    # Keep the legs whose entry point is built; any other failure is fatal.
+    legs, missing = [], []
+    for leg in legs_all:
+        rc = leg["call"]()
+        if rc == fa.FA_ERR_UNSUPPORTED:
+            missing.append(leg["name"])
+            continue
+        if rc != fa.FA_OK:
+            raise fa.FaError(rc)
+        legs.append(leg)
+    torch.cuda.synchronize()
+    if not legs:
+        print("no leg of the hot path is built", file=sys.stderr)
+        sys.exit(1)
+    if any(l["name"] == "bwd_bf16" for l in legs):
+        # The backward consumes the forward's O and LSE: keep the forward first.
+        assert legs[0]["name"] == "fwd_bf16"
+
+    def step(events=None):
+        for leg in legs:
+            if events is not None:
+                events[leg["name"]][0].append(torch.cuda.Event(enable_timing=True))
+                events[leg["name"]][0][-1].record()
+            rc = leg["call"]()
+            if events is not None:
+                events[leg["name"]][1].append(torch.cuda.Event(enable_timing=True))
+                events[leg["name"]][1][-1].record()
+            if rc != fa.FA_OK:
+                raise fa.FaError(rc)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly --steps steps between two synchronisations.
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+
+    # Per-launch durations of every leg (separate pass, same work).
+    events = {l["name"]: ([], []) for l in legs}
+    for _ in range(args.steps):
+        step(events)
+    torch.cuda.synchronize()
+    leg_ms = {n: sum(a.elapsed_time(b) for a, b in zip(*ev)) / len(ev[0])
+              for n, ev in events.items()}
+
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib * 2**20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    ms_per_step = total_ms / args.steps
+    step_flops = sum(l["flops"] for l in legs)
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    leg_report = {}
+    for l in legs:
+        ms = leg_ms[l["name"]]
+        tf = l["flops"] / (ms * 1e-3) / 1e12 if l["flops"] else None
+        leg_report[l["name"]] = {
+            "ms": round(ms, 4),
+            "tflops": round(tf, 2) if tf else None,
+            "frac_of_peak": round(tf / PEAK_TFLOPS[l["dtype"]], 4) if tf else None,
+        }
+
+    dom = max((l for l in legs if l["flops"]), key=lambda l: leg_ms[l["name"]])
+    dom_ms = leg_ms[dom["name"]]
+    achieved = dom["flops"] / (dom_ms * 1e-3) / 1e12
+    traffic = stored_traffic(dom["name"]) if dom["name"] in KERNEL_SOURCES else None
+    roofline = {"bound": "mfma", "kernel": dom["kernel"], "achieved": round(achieved, 2),
+                "peak": PEAK_TFLOPS[dom["dtype"]], "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_TFLOPS[dom["dtype"]], 4),
+                "traffic": traffic}
+
+    dtypes = sorted({l["dtype"] for l in legs if l["flops"]})
+    B, H, N, d = (WORKLOAD[k] for k in "BHNd")
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "+".join(dtypes),
+        "data": "synthetic (seeded i.i.d. N(0,1) Q/K/V/dO)",
+        "config": {"workload": f"attention B={B} H={H} N={N} d={d} non-causal "
+                               f"(bf16 forward sweep, longest sequence)",
+                   "B": B, "H": H, "N": N, "d": d, "causal": False,
+                   "legs": [l["name"] for l in legs], "legs_missing": missing},
+        "legs": leg_report,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline({l["name"] for l in legs}, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
