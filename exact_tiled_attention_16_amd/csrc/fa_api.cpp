@@ -100,7 +100,6 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, float* dq, void* dk, void* dv, void* workspace, int B, int H,
            int N, int d, int dtype, float scale, int causal, void* stream) {
-  (void)stream;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
     return FA_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
@@ -109,8 +108,23 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     return FA_ERR_INVALID;
   if (!valid_dims(B, H, N) || (dtype != FA_BF16 && dtype != FA_FP16)) return FA_ERR_INVALID;
   if (!valid_scale(scale) || (causal != 0 && causal != 1)) return FA_ERR_INVALID;
-  if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
-  return FA_ERR_UNSUPPORTED;
+  if (!supported_d(d) || !fa::bwd_supported(d)) return FA_ERR_UNSUPPORTED;
+  fa::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dsum = static_cast<float*>(workspace);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.N = N;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return launch_status(
+      fa::launch_bwd(a, B, H, d, dtype, causal != 0, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

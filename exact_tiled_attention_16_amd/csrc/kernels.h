@@ -22,4 +22,29 @@ struct FwdArgs {
 hipError_t launch_fwd(const FwdArgs& a, int B, int H, int d, int dtype, bool causal,
                       hipStream_t stream);
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* dsum;       // workspace: rowsum(dO o O), [B][H][N]
+  float* dq;         // fp32 [B][H][N][d], zeroed by the preprocess kernel
+  void* dk;
+  void* dv;
+  int N;
+  int n_ktiles;      // filled in by the launcher
+  float scale;
+  float scale_log2;
+};
+
+// Head dimensions the backward is built for.
+bool bwd_supported(int d);
+
+// Enqueue preprocess + main backward kernels.  Arguments are validated by the
+// caller.
+hipError_t launch_bwd(const BwdArgs& a, int B, int H, int d, int dtype, bool causal,
+                      hipStream_t stream);
+
 }  // namespace fa

@@ -158,3 +158,38 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None,
                   lse.data_ptr(), B, H, N, d, dt, float(scale), int(bool(causal)),
                   _stream(q)))
     return out, lse
+
+
+def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+        dq=None, dk=None, dv=None, workspace=None):
+    """(dQ fp32, dK, dV) of <dout, attention(q, k, v)> given the forward's O and
+    LSE; q, k, v, o, dout are [B, H, N, d] bf16/fp16 device tensors."""
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_tensor(t, name, (B, H, N, d), q.dtype)
+    _check_tensor(lse, "lse", (B, H, N), torch.float32)
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if dq is None:
+        dq = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty_like(k)
+    if dv is None:
+        dv = torch.empty_like(v)
+    _check_tensor(dq, "dq", (B, H, N, d), torch.float32)
+    _check_tensor(dk, "dk", (B, H, N, d), q.dtype)
+    _check_tensor(dv, "dv", (B, H, N, d), q.dtype)
+    need = fa_bwd_workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    _check(fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                  dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                  dv.data_ptr(), workspace.data_ptr(), B, H, N, d, dt, float(scale),
+                  int(bool(causal)), _stream(q)))
+    return dq, dk, dv
