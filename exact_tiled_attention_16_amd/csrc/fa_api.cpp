@@ -59,15 +59,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
       fa::launch_fwd(a, B, H, d, dtype, causal != 0, static_cast<hipStream_t>(stream)));
 }
 
-}  // extern "C"
-
-// Entry points whose kernels are not built yet: validated, then reported as
-// unsupported so that callers fail loudly rather than receive garbage.
-extern "C" {
 
 int fa_quant_fp8(const void* x, int dtype, void* x8, float* scales, const float* signs,
                  float scale_mul, int per_tensor, int B, int H, int N, int d, void* stream) {
-  (void)stream;
   if (!x || !x8 || !scales) return FA_ERR_INVALID;
   if (!aligned16(x) || !aligned16(x8) || !aligned4(scales) || !aligned4(signs))
     return FA_ERR_INVALID;
@@ -75,13 +69,22 @@ int fa_quant_fp8(const void* x, int dtype, void* x8, float* scales, const float*
   if (!valid_dims(B, H, N) || (dtype != FA_BF16 && dtype != FA_FP16)) return FA_ERR_INVALID;
   if (per_tensor != 0 && per_tensor != 1) return FA_ERR_INVALID;
   if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
-  return FA_ERR_UNSUPPORTED;
+  fa::QuantArgs a{};
+  a.x = x;
+  a.x8 = x8;
+  a.scales = scales;
+  a.signs = signs;
+  a.scale_mul = scale_mul;
+  a.N = N;
+  a.nblk = (N + FA_FP8_BLOCK - 1) / FA_FP8_BLOCK;
+  if ((int64_t)B * H * a.nblk > 0x7fffffff) return FA_ERR_INVALID;
+  return launch_status(fa::launch_quant_fp8(a, B, H, d, dtype, per_tensor != 0,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_scale,
                const float* k_scale, const float* v_scale, void* o, float* lse, int B, int H,
                int N, int d, float scale, int causal, void* stream) {
-  (void)stream;
   if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !o) return FA_ERR_INVALID;
   if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o)) return FA_ERR_INVALID;
   if (!aligned4(q_scale) || !aligned4(k_scale) || !aligned4(v_scale) || !aligned4(lse))
@@ -89,7 +92,20 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_sc
   if (!valid_dims(B, H, N) || !valid_scale(scale) || (causal != 0 && causal != 1))
     return FA_ERR_INVALID;
   if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
-  return FA_ERR_UNSUPPORTED;
+  fa::Fp8Args a{};
+  a.q8 = q8;
+  a.k8 = k8;
+  a.v8 = v8;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.o = o;
+  a.lse = lse;
+  a.N = N;
+  a.nblk = (N + FA_FP8_BLOCK - 1) / FA_FP8_BLOCK;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return launch_status(
+      fa::launch_fwd_fp8(a, B, H, d, causal != 0, static_cast<hipStream_t>(stream)));
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {

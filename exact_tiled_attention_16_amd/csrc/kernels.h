@@ -39,6 +39,36 @@ struct BwdArgs {
   float scale_log2;
 };
 
+struct QuantArgs {
+  const void* x;       // [B][H][N][d] bf16 / fp16
+  void* x8;            // [B][H][N][d] e4m3 codes
+  float* scales;       // [B][H][nblk]
+  const float* signs;  // d entries of +-1, or null (no rotation)
+  float scale_mul;
+  int N;
+  int nblk;            // ceil(N / 128)
+};
+
+hipError_t launch_quant_fp8(const QuantArgs& a, int B, int H, int d, int dtype, bool per_tensor,
+                            hipStream_t stream);
+
+struct Fp8Args {
+  const void* q8;
+  const void* k8;
+  const void* v8;
+  const float* q_scale;  // [B][H][nblk], 1/d already folded in for rotated Q
+  const float* k_scale;
+  const float* v_scale;
+  void* o;               // bf16
+  float* lse;
+  int N;
+  int nblk;
+  int n_qtiles;          // filled in by the launcher
+  float scale_log2;
+};
+
+hipError_t launch_fwd_fp8(const Fp8Args& a, int B, int H, int d, bool causal, hipStream_t stream);
+
 // Head dimensions the backward is built for.
 bool bwd_supported(int d);
 

@@ -1,0 +1,200 @@
+// FP8 (e4m3) quantisation with block scales and optional incoherent
+// processing ("FlashAttention-3: Fast and Accurate Attention with Asynchrony
+// and Low-precision", abstract: block quantization and incoherent processing;
+// its reference list points to Hadamard-based incoherence).
+//
+//   x' = H_d (s o x)  when signs are given (H_d: unnormalised Sylvester
+//        Hadamard matrix, applied by the fast Walsh-Hadamard transform in
+//        fp32 with half-widths 1, 2, ..., d/2 in that order; each level maps
+//        the pair (x[i], x[i+h]), i & h == 0, to (x[i] + x[i+h], x[i] - x[i+h]))
+//   scale = amax(|x'| over the block) / 448   (1 when the amax is 0)
+//   code  = e4m3_rne(clamp(x' / scale, -448, 448)),  stored = scale * scale_mul
+//
+// A block is FA_FP8_BLOCK = 128 rows of one (b, h), all d columns.  Each row is
+// held by d/8 consecutive lanes, 8 elements per lane; butterflies of
+// half-width < 8 stay inside a lane, wider ones pair lane t with lane t ^ (h/8).
+#include "common.h"
+#include "kernels.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kBlock = 128;
+constexpr int kThreads = 1024;
+
+template <int DT> __device__ __forceinline__ float elem_to_f32(uint32_t bits16);
+template <> __device__ __forceinline__ float elem_to_f32<0>(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+template <> __device__ __forceinline__ float elem_to_f32<1>(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+// MODE 0: block scales, quantise.  MODE 1: write the block amax only.
+// MODE 2: quantise with the amax found in scales[slot] (per-tensor mode).
+template <int D, int DT, int MODE>
+__global__ void __launch_bounds__(kThreads)
+quant_kernel(QuantArgs a) {
+  constexpr int TPR = D / 8;               // lanes per row
+  constexpr int TASKS = kBlock * TPR;      // 8-element chunks per block
+  static_assert(TASKS % kThreads == 0, "");
+  constexpr int CPT = TASKS / kThreads;
+  static_assert(TPR <= 64, "");
+
+  const int tid = threadIdx.x;
+  const int slot = blockIdx.x;             // (b*H + h) * nblk + blk
+  const int bh = slot / a.nblk;
+  const int blk = slot % a.nblk;
+  const int N = a.N;
+  const int row0 = blk * kBlock;
+  const int64_t base = (int64_t)bh * N * D;
+
+  float x[CPT][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + i * kThreads;
+    const int r = c / TPR;
+    const int col = (c % TPR) * 8;
+    const int row = row0 + r;
+    u32x4_t raw = {0u, 0u, 0u, 0u};
+    if (row < N) raw = ld_global16(static_cast<const uint16_t*>(a.x) + base + (int64_t)row * D + col);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[i][2 * j] = elem_to_f32<DT>(raw[j] & 0xffffu);
+      x[i][2 * j + 1] = elem_to_f32<DT>(raw[j] >> 16);
+    }
+    if (a.signs != nullptr) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[i][e] *= a.signs[col + e];
+      // Half-widths 1, 2, 4: inside the lane.
+#pragma unroll
+      for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if ((e & h) == 0) {
+            const float lo = x[i][e], hi = x[i][e + h];
+            x[i][e] = lo + hi;
+            x[i][e + h] = lo - hi;
+          }
+        }
+      }
+      // Half-widths 8 .. D/2: partner lane t ^ (h/8) within the row's lanes.
+      const int t = c % TPR;
+#pragma unroll
+      for (int hl = 1; hl < TPR; hl <<= 1) {
+        const bool upper = (t & hl) != 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float mine = x[i][e];
+          const float other = __shfl_xor(mine, hl, TPR);
+          x[i][e] = upper ? (other - mine) : (mine + other);
+        }
+      }
+    }
+    if (row < N) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
+    }
+  }
+
+  float block_amax;
+  if (MODE == 2) {
+    block_amax = a.scales[slot];
+  } else {
+    // Workgroup max: wave reduction, then across the 16 waves through LDS.
+    __shared__ float red[kThreads / 64];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    if ((tid & 63) == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    block_amax = red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) block_amax = fmaxf(block_amax, red[w]);
+    if (MODE == 1) {
+      if (tid == 0) a.scales[slot] = block_amax;
+      return;
+    }
+  }
+
+  const float scale = block_amax > 0.f ? block_amax / 448.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + i * kThreads;
+    const int r = c / TPR;
+    const int col = (c % TPR) * 8;
+    const int row = row0 + r;
+    if (row >= N) continue;
+    u32x2_t out;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        y[e] = fminf(fmaxf(x[i][4 * j + e] / scale, -448.0f), 448.0f);
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
+      out[j] = (uint32_t)w;
+    }
+    *reinterpret_cast<u32x2_t*>(static_cast<uint8_t*>(a.x8) + base + (int64_t)row * D + col) = out;
+  }
+  if (MODE == 2) __syncthreads();  // every lane has read scales[slot]
+  if (tid == 0) a.scales[slot] = scale * a.scale_mul;
+}
+
+// Max over n values, written back to all n (one workgroup).
+__global__ void __launch_bounds__(kThreads)
+reduce_max_kernel(float* v, int n) {
+  __shared__ float red[kThreads / 64];
+  float m = 0.f;
+  for (int i = threadIdx.x; i < n; i += kThreads) m = fmaxf(m, v[i]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, red[w]);
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += kThreads) v[i] = m;
+}
+
+template <int D, int DT>
+hipError_t launch_d(const QuantArgs& a, int BH, bool per_tensor, hipStream_t s) {
+  const int64_t grid = (int64_t)BH * a.nblk;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  if (!per_tensor) {
+    hipLaunchKernelGGL((quant_kernel<D, DT, 0>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((quant_kernel<D, DT, 1>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(reduce_max_kernel, dim3(1), dim3(kThreads), 0, s, a.scales, (int)grid);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((quant_kernel<D, DT, 2>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_dtype(const QuantArgs& a, int BH, int d, bool per_tensor, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_d<64, DT>(a, BH, per_tensor, s);
+    case 128: return launch_d<128, DT>(a, BH, per_tensor, s);
+    case 256: return launch_d<256, DT>(a, BH, per_tensor, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_fp8(const QuantArgs& a, int B, int H, int d, int dtype, bool per_tensor,
+                            hipStream_t stream) {
+  const int BH = B * H;
+  return dtype == 0 ? launch_dtype<0>(a, BH, d, per_tensor, stream)
+                    : launch_dtype<1>(a, BH, d, per_tensor, stream);
+}
+
+}  // namespace fa

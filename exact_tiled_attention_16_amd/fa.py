@@ -193,3 +193,56 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
                   dv.data_ptr(), workspace.data_ptr(), B, H, N, d, dt, float(scale),
                   int(bool(causal)), _stream(q)))
     return dq, dk, dv
+
+
+def quant_fp8(x, signs=None, scale_mul: float = 1.0, per_tensor: bool = False,
+              out=None, scales=None):
+    """e4m3 codes (uint8 [B,H,N,d]) and block scales (float32 [B,H,ceil(N/128)])
+    of a bf16/fp16 device tensor; ``signs`` (float32 device tensor of d +-1
+    values) turns on the Hadamard rotation."""
+    torch = _torch()
+    if x.dim() != 4:
+        raise ValueError("x must be [B, H, N, d]")
+    B, H, N, d = x.shape
+    _check_tensor(x, "x", (B, H, N, d), x.dtype)
+    dt = _dtype_code(x)
+    nblk = -(-N // FP8_BLOCK)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, nblk), dtype=torch.float32, device=x.device)
+    _check_tensor(out, "out", (B, H, N, d), torch.uint8)
+    _check_tensor(scales, "scales", (B, H, nblk), torch.float32)
+    sp = None
+    if signs is not None:
+        _check_tensor(signs, "signs", (d,), torch.float32)
+        sp = signs.data_ptr()
+    _check(fa_quant_fp8(x.data_ptr(), dt, out.data_ptr(), scales.data_ptr(), sp,
+                        float(scale_mul), int(bool(per_tensor)), B, H, N, d, _stream(x)))
+    return out, scales
+
+
+def fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False,
+            scale: float | None = None, out=None, lse=None):
+    """O (bf16) and LSE of attention on e4m3 operands from ``quant_fp8``."""
+    torch = _torch()
+    if q8.dim() != 4:
+        raise ValueError("q8 must be [B, H, N, d]")
+    B, H, N, d = q8.shape
+    nblk = -(-N // FP8_BLOCK)
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        _check_tensor(t, name, (B, H, N, d), torch.uint8)
+    for name, t in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        _check_tensor(t, name, (B, H, nblk), torch.float32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    _check_tensor(out, "out", (B, H, N, d), torch.bfloat16)
+    _check_tensor(lse, "lse", (B, H, N), torch.float32)
+    _check(fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_scale.data_ptr(),
+                      k_scale.data_ptr(), v_scale.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                      B, H, N, d, float(scale), int(bool(causal)), _stream(q8)))
+    return out, lse

@@ -49,6 +49,8 @@ __all__ = [
     "quantize_fp8",
     "dequantize_fp8",
     "attention_fwd_fp8",
+    "p_rounding_bound",
+    "p_rounding_rms",
 ]
 
 E4M3_MAX = 448.0
@@ -191,3 +193,65 @@ def attention_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale,
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     return attention_fwd(q, k, v, causal=causal, scale=scale)
+
+
+def p_rounding_bound(q, k, v, causal: bool = False, scale: float | None = None):
+    """Elementwise bound on |O_device - O_exact| for attention whose
+    probabilities are rounded to e4m3 before the second product.
+
+    Arguments are the dequantised operands (fp64 [B, H, N, d]).  The device
+    rounds P~ = exp(s - m_t) (m_t a running maximum, m_t <= the row maximum
+    m) to e4m3; the rounded value differs from P~ by at most 2^-4 P~ when P~
+    is normal (>= 2^-6) and by at most 2^-10 (half the subnormal spacing 2^-9)
+    below that.  After the rescaling to the final maximum the contribution of
+    key j to row i is therefore at most
+        max(2^-4 p_ij |v_j|, 2^-10 |v_j| / l_i),   l_i = sum_j exp(s_ij - m_i) >= 1,
+    so the bound is 2^-4 (P |V|)_i + 2^-10 (sum_j |v_j|) / l_i, plus 2^-8 |O|
+    for the bf16 output rounding and fp32 arithmetic.
+    """
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    bound = np.empty_like(q)
+    for b in range(B):
+        for h in range(H):
+            s = (q[b, h] @ k[b, h].T) * scale
+            if causal:
+                s = np.where(np.arange(N)[None, :] > np.arange(N)[:, None], -np.inf, s)
+            m = s.max(axis=1, keepdims=True)
+            e = np.exp(s - m)
+            l = e.sum(axis=1, keepdims=True)
+            p = e / l
+            av = np.abs(v[b, h])
+            vis = np.isfinite(s).astype(np.float64)
+            o = p @ v[b, h]
+            bound[b, h] = (2.0 ** -4) * (p @ av) + (2.0 ** -10) * (vis @ av) / l \
+                + (2.0 ** -8) * np.abs(o) + 1e-6
+    return bound
+
+
+def p_rounding_rms(q, k, v, causal: bool = False, scale: float | None = None):
+    """Expected RMS of O_device - O_exact over all elements when the e4m3
+    rounding errors of different probabilities are independent and uniform:
+    each contributes at most (2^-4 p_ij)^2 / 3 (normal) or (2^-10 / l_i)^2 / 3
+    (subnormal) times v_jc^2 to the variance of element (i, c).  Arguments as
+    in ``p_rounding_bound``."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    total = 0.0
+    for b in range(B):
+        for h in range(H):
+            s = (q[b, h] @ k[b, h].T) * scale
+            if causal:
+                s = np.where(np.arange(N)[None, :] > np.arange(N)[:, None], -np.inf, s)
+            m = s.max(axis=1, keepdims=True)
+            e = np.exp(s - m)
+            l = e.sum(axis=1, keepdims=True)
+            p = e / l
+            w = np.maximum((2.0 ** -8) * p * p, (2.0 ** -20) / (l * l))
+            w = np.where(np.isfinite(s), w, 0.0)
+            total += float(np.sum(w @ (v[b, h] ** 2))) / 3.0
+    return math.sqrt(total / q.size)

@@ -201,3 +201,32 @@ def test_fp8_attention_close_and_ordering_on_outliers():
     rmse_pt = np.sqrt(np.mean((o_pt - ref) ** 2))
     assert rmse_blk < rmse_pt
     assert rmse_blk < 0.05
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rounding_bounds_hold_for_simulated_rounding(causal):
+    """Round exp(s - m) to e4m3 with the oracle's codec (row maximum as the
+    reference, the case the device reaches once the running maximum settles)
+    and check the result against both bounds."""
+    from oracle.fp8 import p_rounding_bound, p_rounding_rms
+    rng = np.random.default_rng(12)
+    B, H, N, d = 1, 2, 300, 64
+    q, k, v = (rng.standard_normal((B, H, N, d)) for _ in range(3))
+    v[0, 0, 7] *= 10.0
+    scale = 1.0 / 8.0
+    exact, _ = attention_fwd(q, k, v, causal=causal, scale=scale)
+    sim = np.empty_like(exact)
+    for h in range(H):
+        s = (q[0, h] @ k[0, h].T) * scale
+        if causal:
+            s = np.where(np.arange(N)[None, :] > np.arange(N)[:, None], -np.inf, s)
+        m = s.max(axis=1, keepdims=True)
+        pt = np.exp(s - m)
+        l = pt.sum(axis=1, keepdims=True)
+        pr = e4m3_decode(e4m3_encode(pt))
+        sim[0, h] = (pr @ v[0, h]) / l
+    bound = p_rounding_bound(q, k, v, causal=causal, scale=scale)
+    assert np.all(np.abs(sim - exact) <= bound)
+    rms = np.sqrt(np.mean((sim - exact) ** 2))
+    assert rms <= p_rounding_rms(q, k, v, causal=causal, scale=scale)
+    assert rms > 0
