@@ -53,6 +53,11 @@ template <> struct Elem<0> {
     f32x2_t v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
   }
+  // acc + lo + hi of a packed pair (one v_dot2 against (1, 1)).
+  static __device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
+    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair), one, acc, false);
+  }
 };
 
 template <> struct Elem<1> {
@@ -63,6 +68,10 @@ template <> struct Elem<1> {
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     f32x2_t v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+  }
+  static __device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
+    const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pair), one, acc, false);
   }
 };
 
@@ -85,6 +94,15 @@ __device__ __forceinline__ float sum_halves(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// True in every lane when the predicate holds in at least one lane.
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// The running row maximum used as the exp2 reference is only raised when a
+// tile's maximum exceeds it by more than this many log2 units.  Probabilities
+// are then at most 2^kLazyMax and the output / normaliser rescale is skipped
+// for most tiles; O and l share the same reference, so the result is exact.
+constexpr float kLazyMax = 8.0f;
+
 // ---------------------------------------------------------------- memory
 
 __device__ __forceinline__ u32x4_t ld_global16(const void* p) {
@@ -102,6 +120,35 @@ __device__ __forceinline__ u32x4_t ld_lds16(const FA_LDS void* p) {
 __device__ __forceinline__ s16x4_t ld_lds_tr16(const FA_LDS void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       reinterpret_cast<FA_LDS s16x4_t*>(const_cast<FA_LDS void*>(p)));
+}
+
+// Asynchronous global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane i writes bytes [16 i, 16 i + 16) of the 1 KiB block at `lds_block`,
+// which must be the same for the whole wave.  Completion is tracked by the
+// vector-memory counter, not by the LDS counter.
+__device__ __forceinline__ void dma16(const void* src, FA_LDS void* lds_block) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (FA_LDS void*)lds_block, 16, 0, 0);
+}
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Waits until at most PENDING of this wave's vector-memory operations (DMA
+// copies included) are outstanding, then a workgroup barrier makes every
+// wave's completed copies visible.  No memory fence: the asm statements only
+// keep the compiler from moving LDS accesses across.
+template <int PENDING>
+__device__ __forceinline__ void dma_sync() {
+  wait_vmcnt<PENDING>();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // ---------------------------------------------------------------- scheduling
