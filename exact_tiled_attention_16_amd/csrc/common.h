@@ -103,6 +103,13 @@ __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballo
 // for most tiles; O and l share the same reference, so the result is exact.
 constexpr float kLazyMax = 8.0f;
 
+// Variant keyed on the probabilities themselves: the reference is raised when
+// one lane's partial row sum of a tile's probabilities (computed against the
+// current reference) exceeds kLazySum, or is not finite.  Below the bound every
+// probability is at most kLazySum, and the reference never exceeds the running
+// maximum, so it stays exact and needs no per-tile maximum.
+constexpr float kLazySum = 1024.0f;
+
 // ---------------------------------------------------------------- memory
 
 __device__ __forceinline__ u32x4_t ld_global16(const void* p) {
@@ -129,6 +136,40 @@ __device__ __forceinline__ s16x4_t ld_lds_tr16(const FA_LDS void* p) {
 __device__ __forceinline__ void dma16(const void* src, FA_LDS void* lds_block) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                    (FA_LDS void*)lds_block, 16, 0, 0);
+}
+
+// Buffer resource for `bytes` bytes at `base` (wave-uniform): base address in
+// dwords 0-1 (stride 0), byte count in dword 2, format word in dword 3.
+// Loads through it at offsets at or past `bytes` return zeros instead of
+// touching memory.  The fields pass through readfirstlane so that the
+// descriptor lives in scalar registers.
+__device__ __forceinline__ u32x4_t make_rsrc(const void* base, int bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  u32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) & 0xffffu;
+  r[2] = __builtin_amdgcn_readfirstlane((uint32_t)bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// Buffer -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane i
+// reads `voff` bytes into the resource and writes bytes [16 i, 16 i + 16) of the
+// 1 KiB block at `lds_block` (wave-uniform, passed in M0).  Out-of-range lanes
+// write zeros.  Issued as inline assembly on purpose: the compiler cannot
+// prove that later LDS reads miss the copy's destination and would otherwise
+// wait for every copy to land right after issuing it.  Completion is
+// therefore tracked only by the explicit vector-memory waits below, which
+// also order the compiler's own loads correctly (vector-memory operations
+// complete in issue order).
+__device__ __forceinline__ void dma16_buf(u32x4_t r, uint32_t voff, FA_LDS void* lds_block) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_block);
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(r), "s"(m0)
+      : "memory", "m0");
 }
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits

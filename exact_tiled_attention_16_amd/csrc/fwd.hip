@@ -5,22 +5,23 @@
 // running row maximum and normaliser; FlashAttention-3 review page, Appendix B
 // fragment: exp2, row sum and output rescaling between the two products).
 //
-// Work unit: one workgroup = NW waves = 32*NW query rows of one (b, h).  Each
-// wave keeps its 32 query rows in registers for the whole key loop.
+// Work unit: one workgroup = NW waves = 32*QB*NW query rows of one (b, h).
+// Each wave keeps QB blocks of 32 query rows in registers for the whole key
+// loop; every K or V fragment read from LDS feeds QB matrix instructions.
 //
 // Data movement: key and value tiles of BN rows are copied from HBM straight
-// into LDS by the asynchronous global->LDS DMA (no staging registers), into a
-// ring of NS = 4 stages per tensor, three tiles ahead of the tile being
-// consumed; the producers are the computing waves themselves (the pages'
-// asynchronous copies overlapped with compute, FlashAttention-3 abstract).
-// At the end of each tile a wave waits only for the copies the next tile
-// needs, then the workgroup barrier publishes them.  LDS rows are unpadded; the 16-byte
-// chunk index of row r is XOR-ed with swz<D>(r), which keeps both LDS read
-// patterns below free of bank conflicts.
+// into LDS by buffer loads with an LDS destination (no staging registers),
+// into rings of three stages per tensor, two iterations ahead of their use;
+// the producers are the computing waves themselves (the pages' asynchronous
+// copies overlapped with compute, FlashAttention-3 abstract).  At the end of
+// each iteration a wave waits only for the copies the next iteration needs,
+// then the workgroup barrier publishes them.  LDS rows are unpadded; the
+// 16-byte chunk index of row r is XOR-ed with swz<D>(r), which keeps both LDS
+// read patterns below free of bank conflicts.
 //
-// Per tile and wave:
+// Per tile and query block:
 //   S^T = K_j Q^T on 32x32x16 matrix cores (keys are accumulator rows, the
-//     wave's 32 queries columns: one lane owns one query row, so row
+//     block's 32 queries columns: one lane owns one query row, so row
 //     reductions are in-lane plus one exchange with the lane 32 away);
 //   online softmax in the exp2 domain (scores times scale*log2(e)), with the
 //     exp2 reference raised lazily; probabilities rounded to the input type;
@@ -30,10 +31,6 @@
 
 #include "common.h"
 #include "kernels.h"
-
-#ifndef FA_FWD128_NW
-#define FA_FWD128_NW 8  // waves per workgroup of the d = 128 forward
-#endif
 
 namespace fa {
 
@@ -51,27 +48,32 @@ __device__ __forceinline__ int swz(int r) {
     return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 
-// OCC = waves per SIMD the register budget is sized for (2: 256 registers).
-template <int D, int BN, int NW, int OCC, bool CAUSAL, int DT>
+#ifndef FA_FWD_INTERLEAVE
+#define FA_FWD_INTERLEAVE 1  // hand-placed instruction order in the main loop
+#endif
+
+// QB = query blocks of 32 rows per wave; OCC = waves per SIMD the register
+// budget is sized for (1: 512 registers, 2: 256).
+template <int D, int BN, int NW, int QB, int OCC, bool CAUSAL, int DT>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 fwd_kernel(FwdArgs a) {
   using E = Elem<DT>;
   using v8 = typename E::v8;
-  constexpr int BM = 32 * NW;
-  constexpr int NS = 4;              // LDS stages per tensor
-  constexpr int ROWB = 2 * D;        // bytes per LDS row
+  constexpr int WQ = 32 * QB;        // query rows per wave
+  constexpr int BM = WQ * NW;        // query rows per workgroup
+  constexpr int NSTG = 3;            // LDS stages per tensor
+  constexpr int ROWB = 2 * D;        // bytes per row (LDS and HBM)
   constexpr int TILEB = BN * ROWB;   // bytes per tile per tensor
   constexpr int CH_ROW = D / 8;      // 16-byte chunks per row
   static_assert(TILEB % (1024 * NW) == 0, "a tile must split into whole 1 KiB copies per wave");
   constexpr int IPW = TILEB / 1024 / NW;  // copies per wave per tensor per tile
-  constexpr int LPT = 2 * IPW;            // vector-memory ops per wave per tile
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
   constexpr int NKB = BN / 32;
   constexpr int NDB = D / 32;
   constexpr int NDC = D / 16;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NS * TILEB];
-  FA_LDS uint8_t* lds = (FA_LDS uint8_t*)smem;  // K stage s at s*TILEB, V at (NS+s)*TILEB
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NSTG * TILEB];
+  FA_LDS uint8_t* lds = (FA_LDS uint8_t*)smem;  // K stage s at s*TILEB, V at (NSTG+s)*TILEB
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -90,48 +92,59 @@ fwd_kernel(FwdArgs a) {
   const uint16_t* V = static_cast<const uint16_t*>(a.v) + base;
 
   const int q0 = qt * BM;
-  const int qw0 = q0 + wave * 32;
-  const int qrow = qw0 + l32;
+  const int qw0 = q0 + wave * WQ;  // first query row of this wave
   const int kend = CAUSAL ? min(N, q0 + BM) : N;
   const int ntiles = (kend + BN - 1) / BN;
   const float c = a.scale_log2;
 
-  // ---- DMA producer: copy j of this wave fills LDS chunk
-  // (wave*IPW + j)*64 + lane of the tile, i.e. row dma_row[j], and must read
-  // the logical chunk that the swizzle maps there.
-  int dma_row[IPW], dma_col[IPW];
+  // ---- Copies.  Copy jj of this wave fills LDS chunk (wave*IPW + jj)*64 + lane
+  // of the tile, i.e. row p / CH_ROW, and reads the logical chunk that the
+  // swizzle maps there.  Tile t is addressed through a buffer resource that
+  // ends at key N, so rows past the end (the ragged tile, tiles past the last)
+  // arrive as zeros without any clamping.
+  uint32_t dma_voff[IPW];
 #pragma unroll
-  for (int j = 0; j < IPW; ++j) {
-    const int p = (wave * IPW + j) * 64 + lane;
-    dma_row[j] = p / CH_ROW;
-    dma_col[j] = ((p % CH_ROW) ^ swz<D>(p / CH_ROW)) * 8;
+  for (int jj = 0; jj < IPW; ++jj) {
+    const int p = (wave * IPW + jj) * 64 + lane;
+    dma_voff[jj] = (uint32_t)((p / CH_ROW) * ROWB + ((p % CH_ROW) ^ swz<D>(p / CH_ROW)) * 16);
   }
-  auto issue = [&](int t) {
-    const int stage = t % NS;
+  auto issue = [&](const uint16_t* src, int t, FA_LDS uint8_t* stage) {
+    const int rows = min(max(N - t * BN, 0), BN);
+    const u32x4_t r = make_rsrc(src + (int64_t)t * BN * D, rows * ROWB);
 #pragma unroll
-    for (int j = 0; j < IPW; ++j) {
-      const int key = min(t * BN + dma_row[j], N - 1);  // rows past N are masked later
-      const int64_t off = (int64_t)key * D + dma_col[j];
-      dma16(K + off, lds + stage * TILEB + (wave * IPW + j) * 1024);
-      dma16(V + off, lds + (NS + stage) * TILEB + (wave * IPW + j) * 1024);
-    }
+    for (int jj = 0; jj < IPW; ++jj) dma16_buf(r, dma_voff[jj], stage + (wave * IPW + jj) * 1024);
   };
-  // Q^T operand: lane holds query qrow, head-dim slots dc*16 + 8*hl + [0, 8).
-  v8 qf[NDC];
+  // Iteration j copies K of tile j+3 and V of tile j+1 (see the loop below).
+  auto issue_iter = [&](int j, int kst, int vst) {
+    issue(K, j + 3, lds + kst * TILEB);
+    issue(V, j + 1, lds + (NSTG + vst) * TILEB);
+  };
+
+  // Q^T operand of block qb: lane holds query qw0 + 32 qb + l32, head-dim
+  // slots dc*16 + 8*hl + [0, 8).
+  v8 qf[QB][NDC];
 #pragma unroll
-  for (int dc = 0; dc < NDC; ++dc) {
-    u32x4_t raw = {0u, 0u, 0u, 0u};
-    if (qrow < N) raw = ld_global16(Q + (int64_t)qrow * D + dc * 16 + 8 * hl);
-    qf[dc] = __builtin_bit_cast(v8, raw);
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = qw0 + 32 * qb + l32;
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) {
+      u32x4_t raw = {0u, 0u, 0u, 0u};
+      if (qrow < N) raw = ld_global16(Q + (int64_t)qrow * D + dc * 16 + 8 * hl);
+      qf[qb][dc] = __builtin_bit_cast(v8, raw);
+    }
   }
 
-  f32x16_t oacc[NDB];
+  f32x16_t oacc[QB][NDB];
+  float m_run[QB], l_run[QB];  // exp2 reference (log2 units), this lane's share of l
 #pragma unroll
-  for (int i = 0; i < NDB; ++i)
+  for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
-  float m_run = -INFINITY;  // exp2 reference of this lane's row, log2 units
-  float l_run = 0.f;        // this lane's share of the normaliser
+    for (int i = 0; i < NDB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[qb][i][r] = 0.f;
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+  }
 
   // ---- LDS read offsets (bytes within a stage).
   // K operand of S^T: lane reads row kb*32 + l32, head-dim chunk 2*dc + hl.
@@ -156,219 +169,302 @@ fwd_kernel(FwdArgs a) {
         voff[db][hi] = r * ROWB + 16 * ((4 * db + 2 * g2 + (c4 >> 1)) ^ f) + 8 * (c4 & 1);
     }
   }
+  auto ld_k = [&](const FA_LDS uint8_t* ks, int kb, int dc) {
+    return __builtin_bit_cast(v8, ld_lds16(ks + kb * 32 * ROWB + koff[dc]));
+  };
+  auto ld_v = [&](const FA_LDS uint8_t* vs, int cc, int db) {
+    const s16x4_t lo = ld_lds_tr16(vs + cc * 16 * ROWB + voff[db][0]);
+    const s16x4_t hi = ld_lds_tr16(vs + cc * 16 * ROWB + voff[db][1]);
+    const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+    return __builtin_bit_cast(v8, u32x4_t{l2[0], l2[1], h2[0], h2[1]});
+  };
+  // P operand of chunk cc (16 keys): accumulator registers 8*(cc%2)..+7 of
+  // score block cc/2, i.e. keys 16cc + 8*(s/4) + 4*hl + s%4 for slot s; the V
+  // operand is read for the same keys.
+  auto p_frag = [&](const uint32_t (&pw)[NKB][8], int cc) {
+    const int j0 = 4 * (cc & 1);
+    return __builtin_bit_cast(
+        v8, u32x4_t{pw[cc >> 1][j0], pw[cc >> 1][j0 + 1], pw[cc >> 1][j0 + 2], pw[cc >> 1][j0 + 3]});
+  };
 
-  // ---- S: raw scores of tile t (S^T block kb: key rows, query columns);
-  // invisible keys are set to -inf.  MASKED tiles (the ragged last tile, the
-  // causal diagonal) are a separate instantiation so that the common path
-  // carries no masking work.
-  auto phase_s = [&](int t, f32x16_t (&sacc)[NKB], auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    const FA_LDS uint8_t* ks = lds + (t % NS) * TILEB;
+  typedef f32x16_t Scores[QB][NKB];
+  typedef uint32_t Probs[QB][NKB][8];
+
+  // ---- One probability pair: keys (2w, 2w+1) of score block kb against the
+  // exp2 reference -m_neg, rounded and packed; adds the unrounded values to
+  // the lane's fp32 partial sums.
+  auto prob_pair = [&](const f32x16_t& s, int w, float m_neg, float& ps0, float& ps1) {
+    const float p0 = fast_exp2(fmaf(s[2 * w], c, m_neg));
+    const float p1 = fast_exp2(fmaf(s[2 * w + 1], c, m_neg));
+    ps0 += p0;
+    ps1 += p1;
+    return E::pack2(p0, p1);
+  };
+  auto phase_p = [&](const f32x16_t (&sacc)[NKB], uint32_t (&pw)[NKB][8], float m_neg) {
+    float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const v8 kf = __builtin_bit_cast(v8, ld_lds16(ks + kb * 32 * ROWB + koff[dc]));
-        sacc[kb] = E::mfma(kf, qf[dc], sacc[kb]);
-      }
-    }
-    if constexpr (MASKED) {
-      // Register r of block kb holds key t*BN + 4*hl + (kb*32 + 8*(r/4) + r%4);
-      // it is visible iff that constant offset is below `lim`.
-      int lim = N - t * BN - 4 * hl;
-      if (CAUSAL) lim = min(lim, qrow + 1 - t * BN - 4 * hl);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) sacc[kb][r] = -INFINITY;
-    }
+      for (int w = 0; w < 8; ++w) pw[kb][w] = prob_pair(sacc[kb], w, m_neg, ps0, ps1);
+    return ps0 + ps1;
   };
 
-  // ---- SM: online softmax of one tile's scores into packed probabilities.
-  // The exp2 reference m_run is raised only when the tile's maximum exceeds
-  // it by kLazyMax, so the probabilities are computed against the current
-  // reference before the maximum is known and recomputed in the rare raise
-  // branch; the exponentials therefore do not wait for the row reduction.
-  auto phase_sm = [&](f32x16_t (&sacc)[NKB], uint32_t (&pw)[NKB][8]) {
-    auto probs = [&](float m_neg) {
-      float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float p0 = fast_exp2(fmaf(sacc[kb][2 * j], c, m_neg));
-          const float p1 = fast_exp2(fmaf(sacc[kb][2 * j + 1], c, m_neg));
-          pw[kb][j] = E::pack2(p0, p1);
-          ps0 += p0;
-          ps1 += p1;
-        }
-      return ps0 + ps1;  // fp32 sum of the unrounded values
-    };
+  // ---- Reference raise (rare): block qb's probabilities were computed
+  // against the current reference and some lane's partial sum left
+  // [0, kLazySum] (or the row had no reference yet).  Raise every row's
+  // reference to the maximum seen so far, rescale O (which already holds all
+  // earlier tiles) and l, and recompute the tile's probabilities.
+  const uint32_t opaque_zero = (uint32_t)(N >> 31);  // 0; unknown to the compiler
+  auto raise_ref = [&](int qb, const f32x16_t (&sacc)[NKB], uint32_t (&pw)[NKB][8], float& psum) {
+    asm volatile("" ::: "memory");  // keep this path a branch
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    float psum = probs(m_run == -INFINITY ? 0.f : -m_run);
-    // Empty uses pin the speculative results before the branch below;
-    // otherwise the compiler sinks them past it, away from the matrix-core
-    // work they are meant to overlap.
+    mx = max_halves(mx) * c;  // scale > 0, so max and scaling commute
+    const float m_new = fmaxf(m_run[qb], mx);
+    const float alpha = (m_new == m_run[qb]) ? 1.0f : fast_exp2(m_run[qb] - m_new);  // 0 on a first tile
+    m_run[qb] = m_new;
+    l_run[qb] *= alpha;
+#pragma unroll
+    for (int i = 0; i < NDB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if constexpr (OCC == 1) {
+          // With a 512-register budget O belongs in the accumulator
+          // registers; a plain multiply here would pull it into the vector
+          // registers for the whole kernel.
+          float t;
+          asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(t) : "a"(oacc[qb][i][r]));
+          t *= alpha;
+          asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(oacc[qb][i][r]) : "v"(t));
+        } else {
+          oacc[qb][i][r] *= alpha;
+        }
+      }
+    uint32_t fresh[NKB][8];
+    psum = phase_p(sacc, fresh, m_new == -INFINITY ? 0.f : -m_new);
+    // Reading the speculative words here keeps the compiler from moving
+    // their computation past the branch.
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) asm volatile("" ::"v"(pw[kb][j]));
-    asm volatile("" ::"v"(psum));
-    mx = max_halves(mx) * c;  // scale > 0, so max and scaling commute
-    const bool raise = mx > m_run + kLazyMax;
-    if (wave_any(raise)) {
-      // Keeps the compiler from turning this rarely taken branch into
-      // unconditional work on every tile.
-      asm volatile("" ::: "memory");
-      // mx is finite whenever raise holds; alpha = 0 on a row's first tile.
-      const float alpha = raise ? fast_exp2(m_run - mx) : 1.0f;
-      m_run = raise ? mx : m_run;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < NDB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-      psum = probs(m_run == -INFINITY ? 0.f : -m_run);
-    }
-    l_run += psum;
+      for (int w = 0; w < 8; ++w) pw[kb][w] = fresh[kb][w] | (pw[kb][w] & opaque_zero);
   };
-
-  // ---- PV: O^T += V^T P^T, 16 keys per instruction.  Chunk cc of the tile
-  // uses accumulator registers 8*(cc%2)..+7 of block cc/2, i.e. keys
-  // 16cc + 8*(s/4) + 4*hl + s%4 for slot s; the V operand is read for the
-  // same keys.
-  auto phase_pv = [&](int t, const uint32_t (&pw)[NKB][8]) {
-    const FA_LDS uint8_t* vs = lds + (NS + t % NS) * TILEB;
+  auto finish_tile = [&](const Scores& s_cur, Probs& p_cur, float (&psum)[QB]) {
 #pragma unroll
-    for (int cc = 0; cc < BN / 16; ++cc) {
-      const int j0 = 4 * (cc & 1);
-      const v8 pf = __builtin_bit_cast(
-          v8, u32x4_t{pw[cc >> 1][j0], pw[cc >> 1][j0 + 1], pw[cc >> 1][j0 + 2], pw[cc >> 1][j0 + 3]});
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const s16x4_t lo = ld_lds_tr16(vs + cc * 16 * ROWB + voff[db][0]);
-        const s16x4_t hi = ld_lds_tr16(vs + cc * 16 * ROWB + voff[db][1]);
-        const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
-        const v8 vf = __builtin_bit_cast(v8, u32x4_t{l2[0], l2[1], h2[0], h2[1]});
-        oacc[db] = E::mfma(vf, pf, oacc[db]);
-      }
+    for (int qb = 0; qb < QB; ++qb) {
+      if (wave_any(!(psum[qb] <= kLazySum))) raise_ref(qb, s_cur[qb], p_cur[qb], psum[qb]);
+      l_run[qb] += psum[qb];
     }
   };
 
-  // Software pipeline (two stages, the pages' intra-group pipelining): at the
-  // start of iteration j the scores S(j) are in registers and tiles up to j+1
-  // are in LDS.  The iteration issues the copy of tile j+NS-1, computes
-  // S(j+1) on the matrix cores while the softmax of tile j runs on the vector
-  // ALUs (same basic block, so the hardware overlaps them), then O += P(j) V(j).
-  // Tiles [0, t_mask) need no mask and every wave takes part in them, so the
-  // main loop has no branches besides the rare reference raise.
+  // Software pipeline over three tiles (the pages' intra-group pipelining,
+  // one tile deeper than their two-stage listing).  Iteration j
+  //   copies K of tile j+3 and V of tile j+1 into the stages they replace,
+  //   computes S(j+1) = K_{j+1} Q^T          (matrix cores),
+  //   turns S(j) into probabilities P(j)      (vector ALUs),
+  //   accumulates O += P(j-1) V_{j-1}         (matrix cores),
+  // three mutually independent streams, which the hardware overlaps.  A raise
+  // of the reference found on P(j) rescales O after P(j-1) V_{j-1} has been
+  // added: O and l then share the new reference.  At the end of iteration j,
+  // K(j+2) and V(j) must have landed; they were issued one iteration
+  // earlier, so the wait leaves this iteration's copies (2 IPW per wave) in
+  // flight.  Tile t uses K stage t%3 and V stage t%3.
   int t_mask = (N % BN) ? N / BN : ntiles;
   if (CAUSAL) t_mask = min(t_mask, (q0 + 1) / BN);
   t_mask = min(t_mask, ntiles);
-  auto active = [&](int t) { return (qw0 < N) && (!CAUSAL || t * BN <= qw0 + 31); };
 
-  f32x16_t scur[NKB], snxt[NKB];
-  uint32_t pw[NKB][8];
+  Scores sA, sB;
+  Probs pA, pB;
 
-  // Prologue: tiles 0 .. NS-2 in flight; wait for tiles 0 and 1; S(0).
-  for (int t = 0; t < NS - 1 && t < ntiles; ++t) issue(t);
-  if (ntiles > 2)
-    dma_sync<LPT * (NS - 3)>();  // tiles 2 .. NS-2 may stay in flight
-  else
-    dma_sync<0>();
-  if (active(0)) {
-    if (t_mask > 0)
-      phase_s(0, scur, std::false_type{});
-    else
-      phase_s(0, scur, std::true_type{});
-  }
-
-  int j = 0;
-  // Main loop: tiles j and j+1 unmasked, all waves active.
-  for (; j + 1 < t_mask; ++j) {
-    const bool ahead = j + NS - 1 < ntiles;
-    if (ahead) issue(j + NS - 1);  // its stage was last read before the previous barrier
-    phase_s(j + 1, snxt, std::false_type{});
-    phase_sm(scur, pw);
-    phase_pv(j, pw);
+  // One iteration as NSTEP fused steps, each with QB S(j+1) and QB P(j-1) V
+  // matrix instructions sharing one K and one V fragment, and a share of the
+  // probability pairs of P(j); LDS fragments are read PF steps ahead.  A
+  // scheduling barrier after each step keeps the vector work spread evenly
+  // under the matrix work.  DS / DP / DPV select which of the three streams
+  // run (the ragged end and the causal diagonal drop some for some waves);
+  // MS masks S(j+1).  S(j) is in s_cur, P(j-1) in p_prev; S(j+1) goes to
+  // s_nxt and P(j) to p_cur.
+  constexpr int NSTEP = NKB * NDC;  // == (BN / 16) * NDB
+  constexpr int NPAIR = NKB * 8;    // probability pairs per lane, tile and block
+  constexpr int PF = D >= 256 ? 1 : 2;  // fragment prefetch distance in steps
+  auto fused = [&](auto ds_tag, auto ms_tag, auto dp_tag, auto dpv_tag, int j, int st,
+                   const Scores& s_cur, Scores& s_nxt, Probs& p_cur, const Probs& p_prev) {
+    constexpr bool DS = decltype(ds_tag)::value, MS = decltype(ms_tag)::value;
+    constexpr bool DP = decltype(dp_tag)::value, DPV = decltype(dpv_tag)::value;
+    const int st1 = st == 2 ? 0 : st + 1;
+    const int stm = st == 0 ? 2 : st - 1;
+    issue_iter(j, st, st1);
+    const FA_LDS uint8_t* ks = lds + st1 * TILEB;
+    const FA_LDS uint8_t* vs = lds + (NSTG + stm) * TILEB;
+    v8 kfr[PF + 1], vfr[PF + 1];
+    // S(j+1) runs key block by key block (kb-major) and P(j) consumes S(j)
+    // in the same order, so only about half of each score set is live at once.
+    auto load = [&](int step) {
+      if constexpr (DS) kfr[step % (PF + 1)] = ld_k(ks, step / NDC, step % NDC);
+      if constexpr (DPV) vfr[step % (PF + 1)] = ld_v(vs, step / NDB, step % NDB);
+    };
+    if constexpr (DS) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) scur[kb] = snxt[kb];
-    // Tile j+2 must be complete for the next iteration.
-    if (j + NS - 1 < ntiles)
-      dma_sync<LPT * (NS - 3)>();
-    else
-      dma_sync<0>();
-  }
-  // Tail: masked tiles and per-wave activity checks.
-  for (; j < ntiles; ++j) {
-    const bool ahead = j + NS - 1 < ntiles;
-    if (ahead) issue(j + NS - 1);
-    if (j + 1 < ntiles && active(j + 1)) phase_s(j + 1, snxt, std::true_type{});
-    if (active(j)) {
-      phase_sm(scur, pw);
-      phase_pv(j, pw);
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s_nxt[qb][kb][r] = 0.f;
     }
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) scur[kb] = snxt[kb];
-    if (ahead)
-      dma_sync<LPT * (NS - 3)>();
-    else
-      dma_sync<0>();
-  }
-
-  // Epilogue: normalise, round, store; LSE in natural log.
-  const float l_tot = sum_halves(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qrow < N) {
-    uint16_t* orow = static_cast<uint16_t*>(a.o) + base + (int64_t)qrow * D;
+    for (int step = 0; step < PF; ++step) load(step);
+    float m_neg[QB], ps0[QB], ps1[QB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+    for (int qb = 0; qb < QB; ++qb) {
+      m_neg[qb] = -m_run[qb];
+      ps0[qb] = 0.f;
+      ps1[qb] = 0.f;
+    }
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2_t w;
-        w[0] = E::pack2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
-        w[1] = E::pack2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2_t*>(orow + db * 32 + 8 * g + 4 * hl) = w;
+    for (int step = 0; step < NSTEP; ++step) {
+      if (step + PF < NSTEP) load(step + PF);
+      const int slot = step % (PF + 1);
+      const int kb = step / NDC, dc = step % NDC;
+      const int cc = step / NDB, db = step % NDB;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if constexpr (DS) s_nxt[qb][kb] = E::mfma(kfr[slot], qf[qb][dc], s_nxt[qb][kb]);
+        if constexpr (DPV) oacc[qb][db] = E::mfma(vfr[slot], p_frag(p_prev[qb], cc), oacc[qb][db]);
+      }
+      if constexpr (DP) {
+#pragma unroll
+        for (int pr = step * NPAIR / NSTEP; pr < (step + 1) * NPAIR / NSTEP; ++pr)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            p_cur[qb][pr / 8][pr % 8] =
+                prob_pair(s_cur[qb][pr / 8], pr % 8, m_neg[qb], ps0[qb], ps1[qb]);
+      }
+#if FA_FWD_INTERLEAVE
+      __builtin_amdgcn_sched_barrier(0);
+#endif
+    }
+    if constexpr (DS && MS) {
+      // Register r of block kb holds key t*BN + 4*hl + (kb*32 + 8*(r/4) + r%4)
+      // with t = j+1; it is visible iff that constant offset is below `lim`.
+      const int t = j + 1;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        int lim = N - t * BN - 4 * hl;
+        if (CAUSAL) lim = min(lim, qw0 + 32 * qb + l32 + 1 - t * BN - 4 * hl);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s_nxt[qb][kb][r] = -INFINITY;
       }
     }
-    if (hl == 0 && a.lse != nullptr)
-      a.lse[(int64_t)bh * N + qrow] = m_run * kLn2 + __logf(l_tot);
+    if constexpr (DP) {
+      float psum[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) psum[qb] = ps0[qb] + ps1[qb];
+      finish_tile(s_cur, p_cur, psum);
+    }
+    dma_sync<2 * IPW>();
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+
+  // Iterations run uniformly to j = ntiles, with no per-wave branches: a
+  // tile past the last one, or past a wave's causal diagonal, arrives as
+  // zeros (or is masked) so its scores are all -inf, its probabilities
+  // exactly 0 and its P V product exactly 0.
+  //
+  // Prologue: K(0) and K(1) in flight, wait for K(0); iteration -1 computes
+  // S(0) only and issues K(2) and V(0) like any iteration; its closing wait
+  // leaves exactly those in flight, so K(1) has landed for iteration 0.
+  issue(K, 0, lds);
+  issue(K, 1, lds + TILEB);
+  dma_sync<IPW>();
+  fused(T_{}, T_{}, F_{}, F_{}, -1, 2, sB, sA, pB, pA);  // S(0) -> sA
+  fused(T_{}, T_{}, T_{}, F_{}, 0, 0, sA, sB, pA, pB);   // S(1) -> sB, P(0) -> pA
+  // Unmasked iterations two per trip, so that the score and probability
+  // register sets swap roles instead of being copied; then the masked rest.
+  int j = 1, st = 1;
+  for (; j + 2 < t_mask; j += 2) {
+    const int stb = st == 2 ? 0 : st + 1;
+    fused(T_{}, F_{}, T_{}, T_{}, j, st, sB, sA, pB, pA);
+    fused(T_{}, F_{}, T_{}, T_{}, j + 1, stb, sA, sB, pA, pB);
+    st = stb == 2 ? 0 : stb + 1;
+  }
+  for (; j <= ntiles; j += 2) {
+    const int stb = st == 2 ? 0 : st + 1;
+    fused(T_{}, T_{}, T_{}, T_{}, j, st, sB, sA, pB, pA);
+    if (j + 1 > ntiles) break;
+    fused(T_{}, T_{}, T_{}, T_{}, j + 1, stb, sA, sB, pA, pB);
+    st = stb == 2 ? 0 : stb + 1;
+  }
+  wait_vmcnt<0>();  // copies past the last tile must land before LDS is released
+
+  // Epilogue: normalise, round, store; LSE in natural log.
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = qw0 + 32 * qb + l32;
+    const float l_tot = sum_halves(l_run[qb]);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qrow < N) {
+      uint16_t* orow = static_cast<uint16_t*>(a.o) + base + (int64_t)qrow * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2_t w;
+          w[0] = E::pack2(oacc[qb][db][4 * g + 0] * inv, oacc[qb][db][4 * g + 1] * inv);
+          w[1] = E::pack2(oacc[qb][db][4 * g + 2] * inv, oacc[qb][db][4 * g + 3] * inv);
+          *reinterpret_cast<u32x2_t*>(orow + db * 32 + 8 * g + 4 * hl) = w;
+        }
+      }
+      if (hl == 0 && a.lse != nullptr)
+        a.lse[(int64_t)bh * N + qrow] = m_run[qb] * kLn2 + __logf(l_tot);
+    }
   }
 }
 
-template <int D, int BN, int NW, int OCC, bool CAUSAL, int DT>
+// Per head dimension: keys per tile, waves per workgroup, query blocks per
+// wave, waves per SIMD.
+template <int D> struct FwdCfg;
+#ifndef FA_FWD128_QB
+#define FA_FWD128_QB 1
+#endif
+template <> struct FwdCfg<64> { static constexpr int BN = 64, NW = 8, QB = 1, OCC = 2; };
+#if FA_FWD128_QB == 2
+template <> struct FwdCfg<128> { static constexpr int BN = 64, NW = 4, QB = 2, OCC = 1; };
+#else
+template <> struct FwdCfg<128> { static constexpr int BN = 64, NW = 8, QB = 1, OCC = 2; };
+#endif
+template <> struct FwdCfg<256> { static constexpr int BN = 32, NW = 4, QB = 1, OCC = 1; };
+
+template <int D, bool CAUSAL, int DT>
 hipError_t launch_one(const FwdArgs& a, int BH, hipStream_t stream) {
-  constexpr int BM = 32 * NW;
+  using C = FwdCfg<D>;
+  constexpr int BM = 32 * C::QB * C::NW;
   FwdArgs args = a;
   args.n_qtiles = (a.N + BM - 1) / BM;
   const int64_t grid = (int64_t)args.n_qtiles * BH;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_kernel<D, BN, NW, OCC, CAUSAL, DT>), dim3((unsigned)grid),
-                     dim3(NW * 64), 0, stream, args);
+  hipLaunchKernelGGL((fwd_kernel<D, C::BN, C::NW, C::QB, C::OCC, CAUSAL, DT>), dim3((unsigned)grid),
+                     dim3(C::NW * 64), 0, stream, args);
   return hipGetLastError();
 }
 
-template <int D, int BN, int NW, int OCC, int DT>
+template <int D, int DT>
 hipError_t launch_causal(const FwdArgs& a, int BH, bool causal, hipStream_t s) {
-  return causal ? launch_one<D, BN, NW, OCC, true, DT>(a, BH, s)
-                : launch_one<D, BN, NW, OCC, false, DT>(a, BH, s);
+  return causal ? launch_one<D, true, DT>(a, BH, s) : launch_one<D, false, DT>(a, BH, s);
 }
 
 template <int DT>
 hipError_t launch_dtype(const FwdArgs& a, int BH, int d, bool causal, hipStream_t s) {
   switch (d) {
-    case 64: return launch_causal<64, 64, 8, 2, DT>(a, BH, causal, s);
-    case 128: return launch_causal<128, 64, FA_FWD128_NW, 2, DT>(a, BH, causal, s);
-    case 256: return launch_causal<256, 32, 4, 1, DT>(a, BH, causal, s);
+    case 64: return launch_causal<64, DT>(a, BH, causal, s);
+    case 128: return launch_causal<128, DT>(a, BH, causal, s);
+    case 256: return launch_causal<256, DT>(a, BH, causal, s);
     default: return hipErrorInvalidValue;
   }
 }
