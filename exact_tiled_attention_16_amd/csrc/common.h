@@ -155,7 +155,7 @@ __device__ __forceinline__ u32x4_t make_rsrc(const void* base, int bytes) {
 
 // Buffer -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane i
 // reads `voff` bytes into the resource and writes bytes [16 i, 16 i + 16) of the
-// 1 KiB block at `lds_block` (wave-uniform, passed in M0).  Out-of-range lanes
+// 1 KiB block at `lds_block` (wave-uniform, placed in M0 by the compiler).  Out-of-range lanes
 // write zeros.  Issued as inline assembly on purpose: the compiler cannot
 // prove that later LDS reads miss the copy's destination and would otherwise
 // wait for every copy to land right after issuing it.  Completion is
@@ -164,12 +164,7 @@ __device__ __forceinline__ u32x4_t make_rsrc(const void* base, int bytes) {
 // complete in issue order).
 __device__ __forceinline__ void dma16_buf(u32x4_t r, uint32_t voff, FA_LDS void* lds_block) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_block);
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "buffer_load_dwordx4 %0, %1, 0 offen lds"
-      :
-      : "v"(voff), "s"(r), "s"(m0)
-      : "memory", "m0");
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "{m0}"(m0) : "memory");
 }
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits

@@ -53,21 +53,22 @@ __device__ __forceinline__ int swz(int r) {
 #endif
 
 // QB = query blocks of 32 rows per wave; OCC = waves per SIMD the register
-// budget is sized for (1: 512 registers, 2: 256).
-template <int D, int BN, int NW, int QB, int OCC, bool CAUSAL, int DT>
+// budget is sized for (1: 512 registers, 2: 256); NSTG = LDS stages per
+// tensor (2 or 3, see the pipeline description below).
+template <int D, int BN, int NW, int QB, int OCC, int NSTG, bool CAUSAL, int DT>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 fwd_kernel(FwdArgs a) {
   using E = Elem<DT>;
   using v8 = typename E::v8;
   constexpr int WQ = 32 * QB;        // query rows per wave
   constexpr int BM = WQ * NW;        // query rows per workgroup
-  constexpr int NSTG = 3;            // LDS stages per tensor
   constexpr int ROWB = 2 * D;        // bytes per row (LDS and HBM)
   constexpr int TILEB = BN * ROWB;   // bytes per tile per tensor
   constexpr int CH_ROW = D / 8;      // 16-byte chunks per row
   static_assert(TILEB % (1024 * NW) == 0, "a tile must split into whole 1 KiB copies per wave");
   constexpr int IPW = TILEB / 1024 / NW;  // copies per wave per tensor per tile
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+  static_assert(NSTG == 2 || NSTG == 3, "stage count");
   constexpr int NKB = BN / 32;
   constexpr int NDB = D / 32;
   constexpr int NDC = D / 16;
@@ -109,15 +110,24 @@ fwd_kernel(FwdArgs a) {
     dma_voff[jj] = (uint32_t)((p / CH_ROW) * ROWB + ((p % CH_ROW) ^ swz<D>(p / CH_ROW)) * 16);
   }
   auto issue = [&](const uint16_t* src, int t, FA_LDS uint8_t* stage) {
-    const int rows = min(max(N - t * BN, 0), BN);
+    const int rows = t < 0 ? 0 : min(max(N - t * BN, 0), BN);
     const u32x4_t r = make_rsrc(src + (int64_t)t * BN * D, rows * ROWB);
 #pragma unroll
     for (int jj = 0; jj < IPW; ++jj) dma16_buf(r, dma_voff[jj], stage + (wave * IPW + jj) * 1024);
   };
-  // Iteration j copies K of tile j+3 and V of tile j+1 (see the loop below).
-  auto issue_iter = [&](int j, int kst, int vst) {
-    issue(K, j + 3, lds + kst * TILEB);
-    issue(V, j + 1, lds + (NSTG + vst) * TILEB);
+  // Tile t lives in stage t % NSTG of each ring.  Iteration j reads K(j+1)
+  // and V(j-1) and copies K(j+KAHEAD) and V(j+VAHEAD) into the stages they
+  // replace (see the pipeline description below).
+  constexpr int KAHEAD = NSTG == 3 ? 3 : 2;
+  constexpr int VAHEAD = NSTG == 3 ? 1 : 0;
+  constexpr int PENDING = NSTG == 3 ? 2 * IPW : 0;  // copies left in flight at an iteration's end
+  // Stage arithmetic on st = j % NSTG, carried by the loops.
+  auto snext = [](int x) { return x == NSTG - 1 ? 0 : x + 1; };
+  auto sprev = [](int x) { return x == 0 ? NSTG - 1 : x - 1; };
+  auto issue_iter = [&](int j, int st) {
+    // (j + KAHEAD) % NSTG == st; (j + VAHEAD) % NSTG == st + 1 or st.
+    issue(K, j + KAHEAD, lds + st * TILEB);
+    issue(V, j + VAHEAD, lds + (NSTG + (NSTG == 3 ? snext(st) : st)) * TILEB);
   };
 
   // Q^T operand of block qb: lane holds query qw0 + 32 qb + l32, head-dim
@@ -262,16 +272,17 @@ fwd_kernel(FwdArgs a) {
 
   // Software pipeline over three tiles (the pages' intra-group pipelining,
   // one tile deeper than their two-stage listing).  Iteration j
-  //   copies K of tile j+3 and V of tile j+1 into the stages they replace,
+  //   copies K(j+KAHEAD) and V(j+VAHEAD) into the stages they replace,
   //   computes S(j+1) = K_{j+1} Q^T          (matrix cores),
   //   turns S(j) into probabilities P(j)      (vector ALUs),
   //   accumulates O += P(j-1) V_{j-1}         (matrix cores),
   // three mutually independent streams, which the hardware overlaps.  A raise
   // of the reference found on P(j) rescales O after P(j-1) V_{j-1} has been
   // added: O and l then share the new reference.  At the end of iteration j,
-  // K(j+2) and V(j) must have landed; they were issued one iteration
-  // earlier, so the wait leaves this iteration's copies (2 IPW per wave) in
-  // flight.  Tile t uses K stage t%3 and V stage t%3.
+  // K(j+2) and V(j) must have landed for iteration j+1.  With three stages
+  // they were issued one iteration earlier and this iteration's copies stay
+  // in flight; with two stages (half the LDS, so two workgroups fit on a CU)
+  // they were issued at the start of this iteration and the wait drains all.
   int t_mask = (N % BN) ? N / BN : ntiles;
   if (CAUSAL) t_mask = min(t_mask, (q0 + 1) / BN);
   t_mask = min(t_mask, ntiles);
@@ -294,11 +305,9 @@ fwd_kernel(FwdArgs a) {
                    const Scores& s_cur, Scores& s_nxt, Probs& p_cur, const Probs& p_prev) {
     constexpr bool DS = decltype(ds_tag)::value, MS = decltype(ms_tag)::value;
     constexpr bool DP = decltype(dp_tag)::value, DPV = decltype(dpv_tag)::value;
-    const int st1 = st == 2 ? 0 : st + 1;
-    const int stm = st == 0 ? 2 : st - 1;
-    issue_iter(j, st, st1);
-    const FA_LDS uint8_t* ks = lds + st1 * TILEB;
-    const FA_LDS uint8_t* vs = lds + (NSTG + stm) * TILEB;
+    issue_iter(j, st);
+    const FA_LDS uint8_t* ks = lds + snext(st) * TILEB;
+    const FA_LDS uint8_t* vs = lds + (NSTG + sprev(st)) * TILEB;
     v8 kfr[PF + 1], vfr[PF + 1];
     // S(j+1) runs key block by key block (kb-major) and P(j) consumes S(j)
     // in the same order, so only about half of each score set is live at once.
@@ -367,7 +376,7 @@ fwd_kernel(FwdArgs a) {
       for (int qb = 0; qb < QB; ++qb) psum[qb] = ps0[qb] + ps1[qb];
       finish_tile(s_cur, p_cur, psum);
     }
-    dma_sync<2 * IPW>();
+    dma_sync<PENDING>();
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
@@ -381,25 +390,29 @@ fwd_kernel(FwdArgs a) {
   // S(0) only and issues K(2) and V(0) like any iteration; its closing wait
   // leaves exactly those in flight, so K(1) has landed for iteration 0.
   issue(K, 0, lds);
-  issue(K, 1, lds + TILEB);
-  dma_sync<IPW>();
-  fused(T_{}, T_{}, F_{}, F_{}, -1, 2, sB, sA, pB, pA);  // S(0) -> sA
-  fused(T_{}, T_{}, T_{}, F_{}, 0, 0, sA, sB, pA, pB);   // S(1) -> sB, P(0) -> pA
+  if constexpr (NSTG == 3) {
+    issue(K, 1, lds + TILEB);
+    dma_sync<IPW>();
+  } else {
+    dma_sync<0>();
+  }
+  fused(T_{}, T_{}, F_{}, F_{}, -1, NSTG - 1, sB, sA, pB, pA);  // S(0) -> sA
+  fused(T_{}, T_{}, T_{}, F_{}, 0, 0, sA, sB, pA, pB);          // S(1) -> sB, P(0) -> pA
   // Unmasked iterations two per trip, so that the score and probability
   // register sets swap roles instead of being copied; then the masked rest.
-  int j = 1, st = 1;
+  int j = 1, st = 1 % NSTG;
   for (; j + 2 < t_mask; j += 2) {
-    const int stb = st == 2 ? 0 : st + 1;
+    const int stb = snext(st);
     fused(T_{}, F_{}, T_{}, T_{}, j, st, sB, sA, pB, pA);
     fused(T_{}, F_{}, T_{}, T_{}, j + 1, stb, sA, sB, pA, pB);
-    st = stb == 2 ? 0 : stb + 1;
+    st = snext(stb);
   }
   for (; j <= ntiles; j += 2) {
-    const int stb = st == 2 ? 0 : st + 1;
+    const int stb = snext(st);
     fused(T_{}, T_{}, T_{}, T_{}, j, st, sB, sA, pB, pA);
     if (j + 1 > ntiles) break;
     fused(T_{}, T_{}, T_{}, T_{}, j + 1, stb, sA, sB, pA, pB);
-    st = stb == 2 ? 0 : stb + 1;
+    st = snext(stb);
   }
   wait_vmcnt<0>();  // copies past the last tile must land before LDS is released
 
@@ -428,18 +441,21 @@ fwd_kernel(FwdArgs a) {
 }
 
 // Per head dimension: keys per tile, waves per workgroup, query blocks per
-// wave, waves per SIMD.
+// wave, waves per SIMD, LDS stages per tensor.  FA_FWD128_CFG = 1 selects a
+// d = 128 layout with four-wave workgroups and two stages, so that two
+// workgroups share a CU and their barriers do not couple (measured slower
+// than the default on MI355X; kept for comparison).
 template <int D> struct FwdCfg;
-#ifndef FA_FWD128_QB
-#define FA_FWD128_QB 1
+#ifndef FA_FWD128_CFG
+#define FA_FWD128_CFG 0
 #endif
-template <> struct FwdCfg<64> { static constexpr int BN = 64, NW = 8, QB = 1, OCC = 2; };
-#if FA_FWD128_QB == 2
-template <> struct FwdCfg<128> { static constexpr int BN = 64, NW = 4, QB = 2, OCC = 1; };
+template <> struct FwdCfg<64> { static constexpr int BN = 64, NW = 8, QB = 1, OCC = 2, NSTG = 3; };
+#if FA_FWD128_CFG == 1
+template <> struct FwdCfg<128> { static constexpr int BN = 64, NW = 4, QB = 1, OCC = 2, NSTG = 2; };
 #else
-template <> struct FwdCfg<128> { static constexpr int BN = 64, NW = 8, QB = 1, OCC = 2; };
+template <> struct FwdCfg<128> { static constexpr int BN = 64, NW = 8, QB = 1, OCC = 2, NSTG = 3; };
 #endif
-template <> struct FwdCfg<256> { static constexpr int BN = 32, NW = 4, QB = 1, OCC = 1; };
+template <> struct FwdCfg<256> { static constexpr int BN = 32, NW = 4, QB = 1, OCC = 1, NSTG = 3; };
 
 template <int D, bool CAUSAL, int DT>
 hipError_t launch_one(const FwdArgs& a, int BH, hipStream_t stream) {
@@ -449,7 +465,7 @@ hipError_t launch_one(const FwdArgs& a, int BH, hipStream_t stream) {
   args.n_qtiles = (a.N + BM - 1) / BM;
   const int64_t grid = (int64_t)args.n_qtiles * BH;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_kernel<D, C::BN, C::NW, C::QB, C::OCC, CAUSAL, DT>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((fwd_kernel<D, C::BN, C::NW, C::QB, C::OCC, C::NSTG, CAUSAL, DT>), dim3((unsigned)grid),
                      dim3(C::NW * 64), 0, stream, args);
   return hipGetLastError();
 }
