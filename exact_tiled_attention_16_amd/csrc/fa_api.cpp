@@ -110,7 +110,7 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_sc
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   if (!valid_dims(B, H, N) || !supported_d(d)) return 0;
-  return (size_t)B * H * N * sizeof(float);
+  return (size_t)B * H * N * 2 * sizeof(float);  // per row: LSE * log2 e, rowsum(dO o O)
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

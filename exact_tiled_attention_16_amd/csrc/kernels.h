@@ -29,7 +29,7 @@ struct BwdArgs {
   const void* o;
   const void* dout;
   const float* lse;
-  float* dsum;       // workspace: rowsum(dO o O), [B][H][N]
+  float* dsum;       // workspace: [B][H][N] pairs (LSE * log2 e, rowsum(dO o O))
   float* dq;         // fp32 [B][H][N][d], zeroed by the preprocess kernel
   void* dk;
   void* dv;
