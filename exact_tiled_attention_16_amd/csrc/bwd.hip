@@ -9,17 +9,19 @@
 //     dK = scale * dS^T Q,  dQ = scale * dS K.
 //
 // Kernels:
-//   bwd_pre_kernel  per query row: (LSE * log2 e, D) into the workspace.
+//   bwd_pre_kernel  per query row: (-LSE / scale, -D) into the workspace.
 //   bwd_kv_kernel   one workgroup per (b, h, tile of BKV = 32*NW keys); wave w
 //                   owns keys [32 w, 32 w + 32) of the tile and keeps their K
 //                   and V rows, and their dK, dV accumulators, in registers.
 //                   Query tiles of BQ rows (Q, dO and the row statistics)
 //                   stream through a three-stage LDS ring filled by buffer
 //                   loads with an LDS destination.  Per query tile:
-//     A  S = Q K^T and dP = dO V^T on 32x32x16 matrix cores, keys as
-//        accumulator columns (one key per lane), Q and dO read from LDS;
-//     V  P = exp2(S * scale * log2 e - LSE * log2 e), dS = scale * P o (dP - D)
-//        in fp32, rounded to the input type;
+//     A  S - LSE/scale and dP - D on 32x32x16 matrix cores (the accumulators
+//        start from the row statistics), keys as accumulator columns (one key
+//        per lane), Q and dO read from LDS;
+//     V  P = exp2((S - LSE/scale) * scale * log2 e), dS' = P o (dP - D) in
+//        fp32, rounded to the input type (dK = scale * dS'^T Q is scaled
+//        once at the end);
 //     B  dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read from LDS by
 //        transposed 16-bit reads.
 //   bwd_dq_kernel   one workgroup per (b, h, tile of 32*NW queries), built like
@@ -50,12 +52,14 @@ template <> __device__ __forceinline__ float to_f32<1>(uint16_t x) {
   return (float)__builtin_bit_cast(_Float16, x);
 }
 
-// Per row: stat[row] = (LSE * log2 e, sum_c dO[row][c] * O[row][c]).  D/8
+// Per row: stat[row] = (-LSE / scale, -sum_c dO[row][c] * O[row][c]), the
+// starting values of the S and dP accumulators of the backward kernels.  D/8
 // threads per row.
 template <int D, int DT>
 __global__ void __launch_bounds__(256)
 bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-               const float* __restrict__ lse, f32x2_t* __restrict__ stat, int64_t rows) {
+               const float* __restrict__ lse, f32x2_t* __restrict__ stat, int64_t rows,
+               float inv_scale) {
   constexpr int TPR = D / 8;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = gid / TPR;
@@ -72,7 +76,7 @@ bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
-  if (row < rows && c == 0) stat[row] = f32x2_t{lse[row] * kLog2e, acc};
+  if (row < rows && c == 0) stat[row] = f32x2_t{-lse[row] * inv_scale, -acc};
 }
 
 // Same chunk swizzle as the forward's K/V tiles (rows of 2*D bytes): both
@@ -128,7 +132,6 @@ bwd_kv_kernel(BwdArgs a) {
   const int k0 = kt * BKV;
   const int key = k0 + wave * 32 + l32;  // this lane's key (S accumulator column)
   const float c = a.scale_log2;
-  const float sc = a.scale;
 
   // ---- Copies (buffer loads with an LDS destination; rows past N arrive as
   // zeros).  Copy jj of this wave fills LDS chunk (wave*IPW + jj)*64 + lane
@@ -159,7 +162,7 @@ bwd_kv_kernel(BwdArgs a) {
     dma16_buf(r, (uint32_t)lane * 16, sb + 2 * QTB + wave * 1024);
   };
   // Row statistics of query row q of the tile in stage sb: 4 consecutive rows
-  // (q % 4 == 0) as {lse2, D, lse2, D, ...}.
+  // (q % 4 == 0) as {-LSE/scale, -D, -LSE/scale, -D, ...}.
   auto ld_stat4 = [&](const FA_LDS uint8_t* sb, int q, f32x4_t& lo, f32x4_t& hi) {
     constexpr int RPW = BQ / NW;
     const FA_LDS uint8_t* p = sb + 2 * QTB + (q / RPW) * 1024 + (q % RPW) * 8;
@@ -237,15 +240,22 @@ bwd_kv_kernel(BwdArgs a) {
     const FA_LDS uint8_t* os = sb + QTB;
     const int q0 = i * BQ;
 
-    // A: S and dP for every query block (keys as accumulator columns).
+    // A: S - LSE/scale and dP - D for every query block (keys as accumulator
+    // columns).  Register r of block qb is query row qb*32 + 8*(r/4) + 4*hl +
+    // r%4; the accumulators start from that row's statistics.
     f32x16_t sacc[NQB], dpacc[NQB];
     {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sacc[qb][r] = 0.f;
-          dpacc[qb][r] = 0.f;
+        for (int g = 0; g < 4; ++g) {
+          f32x4_t st_lo, st_hi;
+          ld_stat4(sb, qb * 32 + 8 * g + 4 * hl, st_lo, st_hi);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            sacc[qb][4 * g + t] = t < 2 ? st_lo[2 * t] : st_hi[2 * (t - 2)];
+            dpacc[qb][4 * g + t] = t < 2 ? st_lo[2 * t + 1] : st_hi[2 * (t - 2) + 1];
+          }
         }
       constexpr int PF = 2, NST = NQB * NDC;
       v8 qr[PF + 1], orr[PF + 1];
@@ -265,25 +275,21 @@ bwd_kv_kernel(BwdArgs a) {
       }
     }
 
-    // V: probabilities and dS of this tile, fp32, packed as B operands.
+    // V: probabilities and dS' of this tile, fp32, packed as B operands.
 #pragma unroll
     for (int vg = 0; vg < NQB * 4; ++vg) {
       const int qb = vg / 4, g = vg % 4;
       const int qo = qb * 32 + 8 * g + 4 * hl;  // first of this lane's 4 query rows
-      f32x4_t st_lo, st_hi;
-      ld_stat4(sb, qo, st_lo, st_hi);
       float p[4], ds[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const float lse2 = t < 2 ? st_lo[2 * t] : st_hi[2 * (t - 2)];
-        const float dd = t < 2 ? st_lo[2 * t + 1] : st_hi[2 * (t - 2) + 1];
         const int r = 4 * g + t;
-        float pv = fast_exp2(fmaf(sacc[qb][r], c, -lse2));
+        float pv = fast_exp2(sacc[qb][r] * c);
         if constexpr (MASKED) {
           if (key > q0 + qo + t) pv = 0.f;
         }
         p[t] = pv;
-        ds[t] = pv * sc * (dpacc[qb][r] - dd);
+        ds[t] = pv * dpacc[qb][r];
       }
       // Registers 4g..4g+3 are B-operand words (g%2)*2, +1 of chunk g/2.
       pw[qb][g >> 1][2 * (g & 1)] = E::pack2(p[0], p[1]);
@@ -340,7 +346,7 @@ bwd_kv_kernel(BwdArgs a) {
   }
   wait_vmcnt<0>();  // copies past the last tile must land before LDS is released
 
-  // dK (scale already folded into dS) and dV for this lane's key: register r
+  // dK = scale * dS'^T Q and dV for this lane's key: register r
   // of head-dim block db is head dim db*32 + 8*(r/4) + 4*hl + r%4.
   if (key < N) {
     uint16_t* dkrow = static_cast<uint16_t*>(a.dk) + base + (int64_t)key * D;
@@ -351,8 +357,8 @@ bwd_kv_kernel(BwdArgs a) {
       for (int g = 0; g < 4; ++g) {
         const int d0 = db * 32 + 8 * g + 4 * hl;
         u32x2_t w;
-        w[0] = E::pack2(dkacc[db][4 * g + 0], dkacc[db][4 * g + 1]);
-        w[1] = E::pack2(dkacc[db][4 * g + 2], dkacc[db][4 * g + 3]);
+        w[0] = E::pack2(dkacc[db][4 * g + 0] * a.scale, dkacc[db][4 * g + 1] * a.scale);
+        w[1] = E::pack2(dkacc[db][4 * g + 2] * a.scale, dkacc[db][4 * g + 3] * a.scale);
         *reinterpret_cast<u32x2_t*>(dkrow + d0) = w;
         w[0] = E::pack2(dvacc[db][4 * g + 0], dvacc[db][4 * g + 1]);
         w[1] = E::pack2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]);
@@ -368,10 +374,12 @@ bwd_kv_kernel(BwdArgs a) {
 // forward, keys are accumulator rows and the wave's queries are columns (one
 // query per lane), so the row statistics are per-lane scalars.  Per key tile
 // t of BN keys:
-//   S^T = K_t Q^T and dP^T = V_t dO^T (K and V read from LDS as rows),
-//   P^T = exp2(S^T * scale * log2 e - LSE * log2 e),
-//   dS^T = scale * P^T o (dP^T - D), rounded to the input type,
-//   dQ^T += K_t^T dS^T (K read from LDS by transposed reads).
+//   S^T = K_t Q^T and dP^T = V_t dO^T on matrix cores (K and V read from LDS
+//     as rows),
+//   P^T = exp2((S^T - LSE/scale) * scale * log2 e),
+//   dS'^T = P^T o (dP^T - D), rounded to the input type,
+//   dQ^T += K_t^T dS'^T (K read from LDS by transposed reads); dQ = scale *
+//     dQ^T^T is scaled once at the end.
 // K and V tiles stream through a three-stage ring filled by buffer loads with
 // an LDS destination; two waves share each SIMD, so one wave's vector work
 // overlaps the other's matrix work.
@@ -418,7 +426,6 @@ bwd_dq_kernel(BwdArgs a) {
   const int kend = CAUSAL ? min(N, q0 + BM) : N;
   const int ntiles = (kend + BN - 1) / BN;
   const float c = a.scale_log2;
-  const float sc = a.scale;
 
   // Copies: as in the forward (rows past N arrive as zeros).
   uint32_t dma_voff[IPW];
@@ -452,8 +459,8 @@ bwd_dq_kernel(BwdArgs a) {
     of[dc] = __builtin_bit_cast(v8, ro);
   }
   f32x2_t stat = {0.f, 0.f};
-  if (qrow < N) stat = statg[qrow];
-  const float lse2 = stat[0], dd = stat[1];
+  if (qrow < N) stat = statg[qrow];  // (-LSE/scale, -D)
+  const float pbias = stat[0] * c;    // -LSE * log2 e
 
   f32x16_t dqacc[NDB];
 #pragma unroll
@@ -536,12 +543,12 @@ bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int r = 2 * w + u;
-          float pv = fast_exp2(fmaf(sacc[kb][r], c, -lse2));
+          float pv = fast_exp2(fmaf(sacc[kb][r], c, pbias));
           if constexpr (MASKED) {
             const int key = t * BN + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
             if (key > qrow) pv = 0.f;
           }
-          ds2[u] = pv * sc * (dpacc[kb][r] - dd);
+          ds2[u] = pv * (dpacc[kb][r] + stat[1]);
         }
         dw[kb][w] = E::pack2(ds2[0], ds2[1]);
       }
@@ -592,7 +599,8 @@ bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g)
         *reinterpret_cast<f32x4_t*>(dqrow + db * 32 + 8 * g + 4 * hl) =
-            f32x4_t{dqacc[db][4 * g], dqacc[db][4 * g + 1], dqacc[db][4 * g + 2], dqacc[db][4 * g + 3]};
+            f32x4_t{dqacc[db][4 * g], dqacc[db][4 * g + 1], dqacc[db][4 * g + 2], dqacc[db][4 * g + 3]} *
+            a.scale;
   }
 }
 
@@ -605,7 +613,7 @@ hipError_t launch_d(const BwdArgs& a0, int BH, bool causal, hipStream_t s) {
   if (pre_blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((bwd_pre_kernel<D, DT>), dim3((unsigned)pre_blocks), dim3(256), 0, s,
                      static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout),
-                     a.lse, reinterpret_cast<f32x2_t*>(a.dsum), rows);
+                     a.lse, reinterpret_cast<f32x2_t*>(a.dsum), rows, 1.0f / a.scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int BKV = 32 * NW;
