@@ -4,23 +4,27 @@
 // fa_quant_fp8: Q and K rotated by the same signed Hadamard transform (1/d
 // folded into Q's scales), V unrotated, one fp32 scale per 128-row block.
 //
-// Same tiling as the 16-bit forward (query rows in registers, K/V tiles
-// double buffered through LDS, S^T layout with one query per lane), with:
+// Same structure as the 16-bit forward (query rows in registers, K/V tiles
+// copied from HBM into a three-stage LDS ring by buffer loads with an LDS
+// destination, three-stage fused pipeline S(j+1) | softmax(j) | PV(j-1),
+// S^T layout with one query per lane, lazy exp2 reference), with:
 //   * S^T = K8 Q8^T on v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3, fp32 acc);
 //     the product of the query block's and key block's scales, the softmax
 //     scale and log2(e) is one fp32 multiplier per tile (a key tile lies in
 //     one 128-row scale block, a wave's 32 queries likewise);
-//   * probabilities P~ = exp2(s - m) in [0, 1] are rounded to e4m3 (round to
-//     nearest even) for O += P V; the row normaliser is summed from the fp32
-//     P~;
-//   * the output accumulator is kept in units of the current value block's
-//     scale: moving to a tile whose V scale differs multiplies it by
-//     alpha * vs_prev / vs_new (exact in real arithmetic), and the epilogue
-//     multiplies by vs_last / l;
+//   * probabilities P~ = exp2(s - m_ref) are rounded to e4m3 (round to
+//     nearest even) for O += P V; the reference m_ref never exceeds the
+//     running maximum and is raised when some lane's partial row sum of a
+//     tile exceeds kLazySum8, so every P~ stays at most kLazySum8 < 448 (the
+//     e4m3 maximum); the row normaliser is summed from the fp32 P~;
+//   * the output accumulator is kept in units of one value block's scale;
+//     when the next P V product uses another block (every 128 keys) it is
+//     multiplied by vs_old / vs_new, together with any reference raise;
 //   * V8 stays row-major in LDS and is read transposed with ds_read_b64_tr_b8
 //     (inside a 16-lane group, lane j's byte e is byte j%8 of the chunk
-//     addressed by lane 2e + j/8); 8-byte units of a V row are XOR-swizzled
-//     so that the eight rows those reads touch fall in distinct LDS banks.
+//     addressed by lane 2e + j/8); 16-byte chunks of a V row are XOR-swizzled
+//     so that the eight rows those reads touch fall in distinct LDS banks, and
+//     K rows so that sixteen rows read at one column do.
 #include "common.h"
 #include "kernels.h"
 
@@ -40,38 +44,47 @@ __device__ __forceinline__ i32x2_t ld_lds_tr8(const FA_LDS void* p) {
       reinterpret_cast<FA_LDS i32x2_t*>(const_cast<FA_LDS void*>(p)));
 }
 
-// XOR applied to the 8-byte unit index of V row `row` (multiple of 4, so
-// 16-byte chunks stay contiguous and aligned).
+// Probabilities are at most this (P~ is rounded to e4m3, whose maximum is 448).
+constexpr float kLazySum8 = 256.0f;
+
+// XOR applied to the 8-byte unit index of V row `row` (a multiple of 2, i.e.
+// whole 16-byte chunks).
 template <int D>
 __device__ __forceinline__ int v_swz(int row) {
   const int g = ((row >> 1) & 1) | (((row >> 3) & 1) << 1);
   return (4 * g) & (D / 8 - 4);
 }
+// XOR applied to the 16-byte chunk index of K row `row`: rows sharing a
+// 256-byte bank window get distinct chunks.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+  return (row / (256 / D)) & (D / 16 - 1);
+}
 
-template <int D, int BN, int NW, bool CAUSAL>
-__global__ void __launch_bounds__(NW * 64)
-fwd_fp8_kernel(Fp8Args a) {
-  constexpr int NT = NW * 64;
+// The key and value scales are separate read-only, non-aliased arguments so
+// that their per-tile reads can be scalar loads.
+template <int D, int BN, int NW, int OCC, bool CAUSAL>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
   constexpr int BM = 32 * NW;
-  constexpr int KSTR = D + 16;       // bytes; conflict-free 16-byte reads by 16 rows
-  constexpr int VSTR = D;            // bytes; swizzled
-  constexpr int K_BYTES = BN * KSTR;
-  constexpr int STAGE = K_BYTES + BN * VSTR;
-  constexpr int CH_ROW = D / 16;     // 16-byte chunks per row
-  constexpr int CH = BN * CH_ROW;
-  static_assert(CH % NT == 0, "tile chunks must divide evenly over threads");
-  constexpr int CPT = CH / NT;
+  constexpr int NSTG = 3;
+  constexpr int ROWB = D;            // bytes per row
+  constexpr int TILEB = BN * ROWB;
+  constexpr int CH_ROW = D / 16;
+  static_assert(TILEB % (1024 * NW) == 0, "a tile must split into whole 1 KiB copies per wave");
+  constexpr int IPW = TILEB / 1024 / NW;
   static_assert(BN == 64, "one 32x32x64 product per pair of 32-key blocks");
-  static_assert(128 % BN == 0 && 128 % 32 == 0, "tiles inside one scale block");
+  static_assert(128 % BN == 0, "tiles inside one scale block");
+  constexpr int NKB = BN / 32;
   constexpr int NDC = D / 64;        // 64-wide head-dim chunks of S
   constexpr int NDB = D / 32;
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
-  FA_LDS uint8_t* lds = (FA_LDS uint8_t*)smem;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NSTG * TILEB];
+  FA_LDS uint8_t* lds = (FA_LDS uint8_t*)smem;  // K stage s at s*TILEB, V at (NSTG+s)*TILEB
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5;
   const int l32 = lane & 31;
   const int N = a.N;
@@ -85,8 +98,8 @@ fwd_fp8_kernel(Fp8Args a) {
   const uint8_t* K = static_cast<const uint8_t*>(a.k8) + base;
   const uint8_t* V = static_cast<const uint8_t*>(a.v8) + base;
   const float* qsc = a.q_scale + (int64_t)bh * a.nblk;
-  const float* ksc = a.k_scale + (int64_t)bh * a.nblk;
-  const float* vsc = a.v_scale + (int64_t)bh * a.nblk;
+  const float* ksc = k_scale + (int64_t)bh * a.nblk;
+  const float* vsc = v_scale + (int64_t)bh * a.nblk;
 
   const int q0 = qt * BM;
   const int qw0 = q0 + wave * 32;
@@ -94,6 +107,39 @@ fwd_fp8_kernel(Fp8Args a) {
   const int kend = CAUSAL ? min(N, q0 + BM) : N;
   const int ntiles = (kend + BN - 1) / BN;
   const float q_scale = qsc[min(qw0, N - 1) / 128];
+  const float qmul = q_scale * a.scale_log2;
+  // Scales of tile t (clamped past the last block: such tiles are all zero).
+  // These must be scalar loads: a vector load here would be followed by a
+  // wait on the vector-memory counter, which also waits for every tile copy
+  // in flight.
+  const int nblk = a.nblk;
+  auto blk = [&](int t) { return __builtin_amdgcn_readfirstlane(min(max(t, 0) * BN / 128, nblk - 1)); };
+  auto kscale = [&](int t) { return ksc[blk(t)]; };
+  auto vscale = [&](int t) { return vsc[blk(t)]; };
+
+  // ---- Copies.  Copy jj of this wave fills LDS chunk (wave*IPW + jj)*64 +
+  // lane of a tile: row p / CH_ROW; K and V swizzle differently.
+  uint32_t koff_dma[IPW], voff_dma[IPW];
+#pragma unroll
+  for (int jj = 0; jj < IPW; ++jj) {
+    const int p = (wave * IPW + jj) * 64 + lane;
+    const int r = p / CH_ROW, pc = p % CH_ROW;
+    koff_dma[jj] = (uint32_t)(r * ROWB + (pc ^ k_swz<D>(r)) * 16);
+    voff_dma[jj] = (uint32_t)(r * ROWB + (pc ^ (v_swz<D>(r) >> 1)) * 16);
+  }
+  auto issue = [&](const uint8_t* src, int t, FA_LDS uint8_t* stage, const uint32_t (&voff)[IPW]) {
+    const int rows = t < 0 ? 0 : min(max(N - t * BN, 0), BN);
+    const u32x4_t r = make_rsrc(src + (int64_t)max(t, 0) * BN * D, rows * ROWB);
+#pragma unroll
+    for (int jj = 0; jj < IPW; ++jj) dma16_buf(r, voff[jj], stage + (wave * IPW + jj) * 1024);
+  };
+  // Iteration j copies K of tile j+3 and V of tile j+1.
+  auto snext = [](int x) { return x == NSTG - 1 ? 0 : x + 1; };
+  auto sprev = [](int x) { return x == 0 ? NSTG - 1 : x - 1; };
+  auto issue_iter = [&](int j, int st) {
+    issue(K, j + 3, lds + st * TILEB, koff_dma);
+    issue(V, j + 1, lds + (NSTG + snext(st)) * TILEB, voff_dma);
+  };
 
   // Q8^T operand: lane holds query qrow, head-dim bytes dc*64 + 32*hl + [0, 32).
   i32x8_t qf[NDC];
@@ -114,152 +160,221 @@ fwd_fp8_kernel(Fp8Args a) {
   for (int i = 0; i < NDB; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
-  float m_run = -INFINITY;
+  float m_run = -INFINITY;  // exp2 reference, log2 units
   float l_run = 0.f;
-  float vs_cur = 1.f;  // V scale the accumulator is expressed in
+  float vs_acc = vscale(0);  // V scale the accumulator is expressed in
 
-  u32x4_t kreg[CPT], vreg[CPT];
-  auto fetch = [&](int t) {
+  // ---- LDS read offsets.  K rows (A operand of S^T): lane reads row
+  // kb*32 + l32, logical chunks 4*dc + 2*hl + {0, 1}.
+  int koff[NDC][2];
+  {
+    const int f = k_swz<D>(l32);  // equals k_swz of row kb*32 + l32
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NT;
-      const int r = c / CH_ROW;
-      const int col = (c % CH_ROW) * 16;
-      const int key = t * BN + r;
-      if (key < N) {
-        kreg[i] = ld_global16(K + (int64_t)key * D + col);
-        vreg[i] = ld_global16(V + (int64_t)key * D + col);
-      } else {
-        kreg[i] = u32x4_t{0u, 0u, 0u, 0u};
-        vreg[i] = u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto stash = [&](int stage) {
-    FA_LDS uint8_t* ks = lds + stage * STAGE;
-    FA_LDS uint8_t* vs = ks + K_BYTES;
+    for (int dc = 0; dc < NDC; ++dc)
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NT;
-      const int r = c / CH_ROW;
-      const int cc = c % CH_ROW;
-      st_lds16(ks + r * KSTR + cc * 16, kreg[i]);
-      st_lds16(vs + r * VSTR + (((2 * cc) ^ v_swz<D>(r)) * 8), vreg[i]);
-    }
-  };
-
-  // Lane roles in the transposed byte reads: supplier lane 2e + c of each
-  // 16-lane group addresses row e of the group's eight and unit c of two.
+      for (int u = 0; u < 2; ++u) koff[dc][u] = l32 * ROWB + 16 * ((4 * dc + 2 * hl + u) ^ f);
+  }
+  // V^T (A operand of O^T): supplier lane 2e + c of each 16-lane group reads
+  // row tr_row(rd) of the tile and 8-byte unit db*4 + tr_unit.
   const int tr_e = (lane & 15) >> 1;
-  const int tr_c = lane & 1;
-  const int tr_unit = ((lane >> 4) & 1) * 2 + tr_c;   // within a 32-byte column block
-  // Row (within a 64-key tile) of read rd for this supplier: keys in the
-  // order the S^T accumulator hands probabilities to the product.
-  auto tr_row = [&](int rd) { return 16 * rd + 8 * (tr_e >> 2) + 4 * hl + (tr_e & 3); };
-
-  fetch(0);
-  stash(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int stage = t & 1;
-    if (t + 1 < ntiles) fetch(t + 1);
-    const int kbase = t * BN;
-    const bool active = (qw0 < N) && (!CAUSAL || kbase <= qw0 + 31);
-    if (active) {
-      const FA_LDS uint8_t* ks = lds + stage * STAGE;
-      const FA_LDS uint8_t* vs = ks + K_BYTES;
-      const float k_scale = ksc[kbase / 128];
-      const float v_scale = vsc[kbase / 128];
-      const float mult = q_scale * k_scale * a.scale_log2;
-
-      f32x16_t sacc[2];
+  const int tr_unit = ((lane >> 4) & 1) * 2 + (lane & 1);
+  int voff[NDB][4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+  for (int rd = 0; rd < 4; ++rd) {
+    const int row = 16 * rd + 8 * (tr_e >> 2) + 4 * hl + (tr_e & 3);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+    for (int db = 0; db < NDB; ++db)
+      voff[db][rd] = row * ROWB + (((db * 4 + tr_unit) ^ v_swz<D>(row)) * 8);
+  }
+  auto ld_k = [&](const FA_LDS uint8_t* ks, int kb, int dc) {
+    const FA_LDS uint8_t* p = ks + kb * 32 * ROWB;
+    const u32x4_t lo = ld_lds16(p + koff[dc][0]), hi = ld_lds16(p + koff[dc][1]);
+    return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  auto ld_v = [&](const FA_LDS uint8_t* vs, int db) {
+    i32x8_t vf;
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const FA_LDS uint8_t* p = ks + (kb * 32 + l32) * KSTR + dc * 64 + 32 * hl;
-          const u32x4_t lo = ld_lds16(p), hi = ld_lds16(p + 16);
-          const i32x8_t kf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                              (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          sacc[kb] = mfma_fp8(kf, qf[dc], sacc[kb]);
-        }
-      }
+    for (int rd = 0; rd < 4; ++rd) {
+      const i32x2_t v2 = ld_lds_tr8(vs + voff[db][rd]);
+      vf[2 * rd] = v2[0];
+      vf[2 * rd + 1] = v2[1];
+    }
+    return vf;
+  };
 
-      const bool need_mask = (kbase + BN > N) || (CAUSAL && kbase + BN - 1 > qw0);
+  typedef f32x16_t Scores[NKB];
+  typedef int Probs[8];  // P^T operand: byte s = 16*kb + r holds key 32*kb + 8*(r/4) + 4*hl + r%4
+
+  // ---- Probabilities of one tile (scores already multiplied to log2 units
+  // by mul) against the reference -m_neg, packed as e4m3; returns the lane's
+  // fp32 sum of the unrounded values.
+  auto phase_p = [&](const Scores& s, Probs& pw, float mul, float m_neg) {
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const f32x16_t& sb = s[w >> 2];
+      const int r0 = 4 * (w & 3);
+      float p[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) p[u] = fast_exp2(fmaf(sb[r0 + u], mul, m_neg));
+      ps0 += p[0] + p[2];
+      ps1 += p[1] + p[3];
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      pw[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
+    }
+    return ps0 + ps1;
+  };
+
+  // ---- End of a tile: raise the reference if the tile's probabilities left
+  // [0, kLazySum8] (or the row had none), and re-express O in the V scale of
+  // the next P V product.  O already holds P(j-1) V(j-1).
+  const uint32_t opaque_zero = (uint32_t)(N >> 31);
+  auto finish_tile = [&](const Scores& s, Probs& pw, float mul, float psum, float vs_next) {
+    float alpha = 1.0f;
+    if (wave_any(!(psum <= kLazySum8))) {
+      asm volatile("" ::: "memory");
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float s = sacc[kb][r] * mult;
-          if (need_mask) {
-            const int key = kbase + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            if (key >= N || (CAUSAL && key > qrow)) s = -INFINITY;
-          }
-          sacc[kb][r] = s;
-          mx = fmaxf(mx, s);
-        }
-      }
-      mx = max_halves(mx);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = max_halves(mx) * mul;  // mul > 0
       const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float psum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(sacc[kb][r] - m_use);
-          sacc[kb][r] = p;
-          psum += p;
-        }
-      }
-      l_run = l_run * alpha + psum;
+      alpha = (m_new == m_run) ? 1.0f : fast_exp2(m_run - m_new);
       m_run = m_new;
-      const float ofac = alpha * (vs_cur / v_scale);
-      vs_cur = v_scale;
+      l_run *= alpha;
+      Probs fresh;
+      psum = phase_p(s, fresh, mul, m_new == -INFINITY ? 0.f : -m_new);
+#pragma unroll
+      for (int w = 0; w < 8; ++w) pw[w] = (int)((uint32_t)fresh[w] | ((uint32_t)pw[w] & opaque_zero));
+    }
+    l_run += psum;
+    const float f = alpha * (vs_acc / vs_next);
+    if (f != 1.0f) {  // wave-uniform: alpha is 1 unless a raise happened
+      asm volatile("" ::: "memory");
 #pragma unroll
       for (int i = 0; i < NDB; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= ofac;
-
-      // P^T operand: byte s = 16*kb + r holds the probability of key
-      // 32*kb + 8*(r/4) + 4*hl + r%4.
-      i32x8_t pf;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const int s0 = 4 * w;
-        const f32x16_t& sb = sacc[s0 >> 4];
-        const int r0 = s0 & 15;
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(sb[r0], sb[r0 + 1], 0, false);
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(sb[r0 + 2], sb[r0 + 3], word, true);
-        pf[w] = word;
-      }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int unit = db * 4 + tr_unit;
-        i32x8_t vf;
-#pragma unroll
-        for (int rd = 0; rd < 4; ++rd) {
-          const int row = tr_row(rd);
-          const i32x2_t v2 = ld_lds_tr8(vs + row * VSTR + ((unit ^ v_swz<D>(row)) * 8));
-          vf[2 * rd] = v2[0];
-          vf[2 * rd + 1] = v2[1];
+        for (int r = 0; r < 16; ++r) {
+          if constexpr (OCC == 1) {
+            float t;
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(t) : "a"(oacc[i][r]));
+            t *= f;
+            asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(oacc[i][r]) : "v"(t));
+          } else {
+            oacc[i][r] *= f;
+          }
         }
-        oacc[db] = mfma_fp8(vf, pf, oacc[db]);
-      }
     }
-    if (t + 1 < ntiles) stash(stage ^ 1);
-    __syncthreads();
+    vs_acc = vs_next;
+  };
+
+  // Fused iteration (see the 16-bit forward): NSTEP steps, each with one
+  // S(j+1) and one P(j-1) V matrix instruction and a share of the
+  // probability words of P(j).
+  constexpr int NS_S = NKB * NDC, NS_PV = NDB;
+  constexpr int NSTEP = NS_S > NS_PV ? NS_S : NS_PV;
+  auto fused = [&](auto ds_tag, auto ms_tag, auto dp_tag, auto dpv_tag, int j, int st,
+                   const Scores& s_cur, Scores& s_nxt, Probs& p_cur, const Probs& p_prev) {
+    constexpr bool DS = decltype(ds_tag)::value, MS = decltype(ms_tag)::value;
+    constexpr bool DP = decltype(dp_tag)::value, DPV = decltype(dpv_tag)::value;
+    issue_iter(j, st);
+    const FA_LDS uint8_t* ks = lds + snext(st) * TILEB;
+    const FA_LDS uint8_t* vs = lds + (NSTG + sprev(st)) * TILEB;
+    const float mul = qmul * kscale(j);  // tile j's scores to log2 units
+    const float m_neg = -m_run;
+    if constexpr (DS) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s_nxt[kb][r] = 0.f;
+    }
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int step = 0; step < NSTEP; ++step) {
+      if constexpr (DS) {
+        if (step < NS_S) {
+          const int kb = step / NDC, dc = step % NDC;
+          s_nxt[kb] = mfma_fp8(ld_k(ks, kb, dc), qf[dc], s_nxt[kb]);
+        }
+      }
+      if constexpr (DPV) {
+        if (step < NS_PV) {
+          const i32x8_t pf = {p_prev[0], p_prev[1], p_prev[2], p_prev[3],
+                              p_prev[4], p_prev[5], p_prev[6], p_prev[7]};
+          oacc[step] = mfma_fp8(ld_v(vs, step), pf, oacc[step]);
+        }
+      }
+      if constexpr (DP) {
+#pragma unroll
+        for (int w = step * 8 / NSTEP; w < (step + 1) * 8 / NSTEP; ++w) {
+          const f32x16_t& sb = s_cur[w >> 2];
+          const int r0 = 4 * (w & 3);
+          float p[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) p[u] = fast_exp2(fmaf(sb[r0 + u], mul, m_neg));
+          ps0 += p[0] + p[2];
+          ps1 += p[1] + p[3];
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+          p_cur[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
+        }
+      }
+      if constexpr (DS && DP && DPV && OCC > 1) {
+        if (step == 0) __builtin_amdgcn_s_setprio(1);
+        if (step == NSTEP / 2) __builtin_amdgcn_s_setprio(0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (DS && MS) {
+      const int t = j + 1;
+      int lim = N - t * BN - 4 * hl;
+      if (CAUSAL) lim = min(lim, qrow + 1 - t * BN - 4 * hl);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s_nxt[kb][r] = -INFINITY;
+    }
+    if constexpr (DP) finish_tile(s_cur, p_cur, mul, ps0 + ps1, vscale(j));
+    dma_sync<2 * IPW>();
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+
+  int t_mask = (N % BN) ? N / BN : ntiles;
+  if (CAUSAL) t_mask = min(t_mask, (q0 + 1) / BN);
+  t_mask = min(t_mask, ntiles);
+
+  Scores sA, sB;
+  Probs pA, pB;
+
+  // Prologue and iterations as in the 16-bit forward: tiles past the last one
+  // (or past a wave's causal diagonal) come out fully masked, so their
+  // probabilities and P V products are exactly zero.
+  issue(K, 0, lds, koff_dma);
+  issue(K, 1, lds + TILEB, koff_dma);
+  dma_sync<IPW>();
+  fused(T_{}, T_{}, F_{}, F_{}, -1, NSTG - 1, sB, sA, pB, pA);  // S(0) -> sA
+  fused(T_{}, T_{}, T_{}, F_{}, 0, 0, sA, sB, pA, pB);          // S(1) -> sB, P(0) -> pA
+  int j = 1, st = 1;
+  for (; j + 2 < t_mask; j += 2) {
+    const int stb = snext(st);
+    fused(T_{}, F_{}, T_{}, T_{}, j, st, sB, sA, pB, pA);
+    fused(T_{}, F_{}, T_{}, T_{}, j + 1, stb, sA, sB, pA, pB);
+    st = snext(stb);
   }
+  for (; j <= ntiles; j += 2) {
+    const int stb = snext(st);
+    fused(T_{}, T_{}, T_{}, T_{}, j, st, sB, sA, pB, pA);
+    if (j + 1 > ntiles) break;
+    fused(T_{}, T_{}, T_{}, T_{}, j + 1, stb, sA, sB, pA, pB);
+    st = snext(stb);
+  }
+  wait_vmcnt<0>();
 
   const float l_tot = sum_halves(l_run);
-  const float inv = l_tot > 0.f ? vs_cur / l_tot : 0.f;
+  const float inv = l_tot > 0.f ? vs_acc / l_tot : 0.f;
   if (qrow < N) {
     uint16_t* orow = static_cast<uint16_t*>(a.o) + base + (int64_t)qrow * D;
 #pragma unroll
@@ -277,21 +392,21 @@ fwd_fp8_kernel(Fp8Args a) {
   }
 }
 
-template <int D, int NW, bool CAUSAL>
+template <int D, int NW, int OCC, bool CAUSAL>
 hipError_t launch_one(const Fp8Args& a0, int BH, hipStream_t s) {
   constexpr int BM = 32 * NW;
   Fp8Args a = a0;
   a.n_qtiles = (a.N + BM - 1) / BM;
   const int64_t grid = (int64_t)a.n_qtiles * BH;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_fp8_kernel<D, 64, NW, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                     s, a);
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, 64, NW, OCC, CAUSAL>), dim3((unsigned)grid),
+                     dim3(NW * 64), 0, s, a, a.k_scale, a.v_scale);
   return hipGetLastError();
 }
 
-template <int D, int NW>
+template <int D, int NW, int OCC>
 hipError_t launch_d(const Fp8Args& a, int BH, bool causal, hipStream_t s) {
-  return causal ? launch_one<D, NW, true>(a, BH, s) : launch_one<D, NW, false>(a, BH, s);
+  return causal ? launch_one<D, NW, OCC, true>(a, BH, s) : launch_one<D, NW, OCC, false>(a, BH, s);
 }
 
 }  // namespace
@@ -299,9 +414,9 @@ hipError_t launch_d(const Fp8Args& a, int BH, bool causal, hipStream_t s) {
 hipError_t launch_fwd_fp8(const Fp8Args& a, int B, int H, int d, bool causal, hipStream_t stream) {
   const int BH = B * H;
   switch (d) {
-    case 64: return launch_d<64, 4>(a, BH, causal, stream);
-    case 128: return launch_d<128, 8>(a, BH, causal, stream);
-    case 256: return launch_d<256, 4>(a, BH, causal, stream);
+    case 64: return launch_d<64, 4, 2>(a, BH, causal, stream);
+    case 128: return launch_d<128, 8, 2>(a, BH, causal, stream);
+    case 256: return launch_d<256, 4, 1>(a, BH, causal, stream);
     default: return hipErrorInvalidValue;
   }
 }
