@@ -274,7 +274,8 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   // S(j+1) and one P(j-1) V matrix instruction and a share of the
   // probability words of P(j).
   constexpr int NS_S = NKB * NDC, NS_PV = NDB;
-  constexpr int NSTEP = NS_S > NS_PV ? NS_S : NS_PV;
+  constexpr int NSTEP = (NS_S + NS_PV) / 2;
+  static_assert((NS_S + NS_PV) % 2 == 0, "two matrix instructions per step");
   auto fused = [&](auto ds_tag, auto ms_tag, auto dp_tag, auto dpv_tag, int j, int st,
                    const Scores& s_cur, Scores& s_nxt, Probs& p_cur, const Probs& p_prev) {
     constexpr bool DS = decltype(ds_tag)::value, MS = decltype(ms_tag)::value;
@@ -291,19 +292,24 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
         for (int r = 0; r < 16; ++r) s_nxt[kb][r] = 0.f;
     }
     float ps0 = 0.f, ps1 = 0.f;
+    // The P(j-1) V products come first and the S(j+1) products last, so O is
+    // complete when the end of the tile may rescale it, while S(j+1) is not
+    // needed before the next iteration.
+    const i32x8_t pf = {p_prev[0], p_prev[1], p_prev[2], p_prev[3],
+                        p_prev[4], p_prev[5], p_prev[6], p_prev[7]};
 #pragma unroll
     for (int step = 0; step < NSTEP; ++step) {
-      if constexpr (DS) {
-        if (step < NS_S) {
-          const int kb = step / NDC, dc = step % NDC;
-          s_nxt[kb] = mfma_fp8(ld_k(ks, kb, dc), qf[dc], s_nxt[kb]);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int m = 2 * step + u;  // matrix instruction index: PV first, then S
+        if constexpr (DPV) {
+          if (m < NS_PV) oacc[m] = mfma_fp8(ld_v(vs, m), pf, oacc[m]);
         }
-      }
-      if constexpr (DPV) {
-        if (step < NS_PV) {
-          const i32x8_t pf = {p_prev[0], p_prev[1], p_prev[2], p_prev[3],
-                              p_prev[4], p_prev[5], p_prev[6], p_prev[7]};
-          oacc[step] = mfma_fp8(ld_v(vs, step), pf, oacc[step]);
+        if constexpr (DS) {
+          if (m >= NS_PV && m - NS_PV < NS_S) {
+            const int kb = (m - NS_PV) / NDC, dc = (m - NS_PV) % NDC;
+            s_nxt[kb] = mfma_fp8(ld_k(ks, kb, dc), qf[dc], s_nxt[kb]);
+          }
         }
       }
       if constexpr (DP) {
