@@ -140,7 +140,7 @@ def build_legs(torch, fa, dev):
     # One fa_bwd call launches three kernels back to back; the leg is timed
     # (and its roofline reported) as that one launch sequence.
     legs.append(dict(name="bwd_bf16", call=bwd_call, flops=2.5 * fwd_flops(B, H, N, d),
-                     dtype="bf16", kernel="bwd_pre_kernel+bwd_kv_kernel+bwd_dq_kernel"))
+                     dtype="bf16", kernel="bwd_pre_kernel+bwd_kv2_kernel+bwd_dq_kernel"))
     return legs
 
 

@@ -9,28 +9,28 @@
 //     dK = scale * dS^T Q,  dQ = scale * dS K.
 //
 // Kernels:
-//   bwd_pre_kernel  per query row: (-LSE / scale, -D) into the workspace.
-//   bwd_kv_kernel   one workgroup per (b, h, tile of BKV = 32*NW keys); wave w
-//                   owns keys [32 w, 32 w + 32) of the tile and keeps their K
-//                   and V rows, and their dK, dV accumulators, in registers.
-//                   Query tiles of BQ rows (Q, dO and the row statistics)
-//                   stream through a three-stage LDS ring filled by buffer
-//                   loads with an LDS destination.  Per query tile:
-//     A  S - LSE/scale and dP - D on 32x32x16 matrix cores (the accumulators
-//        start from the row statistics), keys as accumulator columns (one key
-//        per lane), Q and dO read from LDS;
-//     V  P = exp2((S - LSE/scale) * scale * log2 e), dS' = P o (dP - D) in
-//        fp32, rounded to the input type (dK = scale * dS'^T Q is scaled
-//        once at the end);
-//     B  dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read from LDS by
-//        transposed 16-bit reads.
+//   bwd_pre_kernel  per query row: -LSE / scale and -D into two planes of the
+//                   workspace (all rows of one, then all rows of the other).
+//   bwd_kv2_kernel  one workgroup of 8 waves per (b, h, tile of 128 keys); the
+//                   four 32-key blocks each get two waves that share a SIMD:
+//                   one keeps the block's K rows and dV accumulator (S, P,
+//                   dV^T += dO^T P), the other its V rows and dK accumulator
+//                   (dP, dS = P o (dP - D), dK^T += Q^T dS); P passes between
+//                   them through LDS in fp32.  Query tiles of 64 rows (Q, dO,
+//                   row statistics) stream through a three-stage LDS ring
+//                   filled by buffer loads with an LDS destination.  Keys are
+//                   accumulator columns (one key per lane); Q and dO are read
+//                   from LDS as rows (S, dP) and by transposed 16-bit reads
+//                   (dV, dK).  The S and dP accumulators start from the row
+//                   statistics, and dK = scale * dS^T Q is scaled once at the
+//                   end.
 //   bwd_dq_kernel   one workgroup per (b, h, tile of 32*NW queries), built like
 //                   the forward: Q and dO rows stay in registers, K and V tiles
 //                   stream through a three-stage LDS ring; per key tile it
 //                   recomputes S^T = K Q^T and dP^T = V dO^T, forms dS^T and
 //                   accumulates dQ^T += K^T dS^T in registers, written once at
 //                   the end.  Recomputing two products costs 2/5 more matrix
-//                   work than accumulating dQ with atomics from bwd_kv_kernel,
+//                   work than accumulating dQ with atomics from the dK/dV pass,
 //                   whose fp32 atomic traffic (every key tile adds a full dQ
 //                   tile) is bound by the L2 atomic units.
 //   Rows past N (queries or keys) arrive as zeros; every product they enter
@@ -39,6 +39,15 @@
 
 #include "common.h"
 #include "kernels.h"
+
+// LDS fragments read ahead of the matrix products in bwd_kv2_kernel: row
+// reads (S / dP) and transposed reads (dV / dK).
+#ifndef FA_KV2_PF_ROW
+#define FA_KV2_PF_ROW 2
+#endif
+#ifndef FA_KV2_PF_TR
+#define FA_KV2_PF_TR 2
+#endif
 
 namespace fa {
 
@@ -52,13 +61,13 @@ template <> __device__ __forceinline__ float to_f32<1>(uint16_t x) {
   return (float)__builtin_bit_cast(_Float16, x);
 }
 
-// Per row: stat[row] = (-LSE / scale, -sum_c dO[row][c] * O[row][c]), the
-// starting values of the S and dP accumulators of the backward kernels.  D/8
-// threads per row.
+// Per row: stat[row] = -LSE / scale and stat[rows + row] = -sum_c dO[row][c]
+// * O[row][c], the starting values of the S and dP accumulators of the
+// backward kernels.  D/8 threads per row.
 template <int D, int DT>
 __global__ void __launch_bounds__(256)
 bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-               const float* __restrict__ lse, f32x2_t* __restrict__ stat, int64_t rows,
+               const float* __restrict__ lse, float* __restrict__ stat, int64_t rows,
                float inv_scale) {
   constexpr int TPR = D / 8;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -76,7 +85,10 @@ bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
-  if (row < rows && c == 0) stat[row] = f32x2_t{-lse[row] * inv_scale, -acc};
+  if (row < rows && c == 0) {
+    stat[row] = -lse[row] * inv_scale;
+    stat[rows + row] = -acc;
+  }
 }
 
 // Same chunk swizzle as the forward's K/V tiles (rows of 2*D bytes): both
@@ -89,32 +101,56 @@ __device__ __forceinline__ int swz(int r) {
     return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 
-template <int D, int NW, int BQ, bool CAUSAL, int DT>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-bwd_kv_kernel(BwdArgs a) {
+
+
+// Key-stationary dK/dV with two wave roles per 32-key block, so that two
+// waves share each SIMD and one's vector work overlaps the other's matrix
+// work.  One workgroup = 8 waves = BKV = 128 keys; wave w takes key block
+// w % 4 (waves w and w + 4 share a SIMD) and role w / 4:
+//   role 0 (S side):  S - LSE/scale = Q K^T + stat, P = exp2(. * scale * log2 e)
+//                     (causal mask), P to LDS in fp32, dV^T += dO^T P;
+//   role 1 (dP side): dP - D = dO V^T + stat, dS' = P o (dP - D) once P is
+//                     published, dK^T += Q^T dS'.
+// Each wave keeps only its side's stationary operand (K or V rows) and
+// accumulator (dV or dK): half of what one wave holding both needs.  The dK
+// products of a query tile run one tile late, in the first phase of the next
+// tile, where they fill the matrix unit while the S side computes P:
+//   phase 1: role 0 S(i), P(i) to LDS     | role 1 dP(i), dK += dS'(i-1)
+//   barrier (tile i+1 landed), copy of tile i+2 into the stage of tile i-1
+//   phase 2: role 0 dV += P(i)            | role 1 dS'(i) from P(i)
+//            both: row statistics of tile i+1 into the S / dP accumulators
+//   barrier (P(i) read)
+// Query tiles of BQ rows (Q, dO, row statistics) stream through a
+// three-stage ring.
+template <int D, int BQ, bool CAUSAL, int DT>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_kv2_kernel(BwdArgs a) {
   using E = Elem<DT>;
   using v8 = typename E::v8;
-  constexpr int BKV = 32 * NW;       // keys per workgroup
-  constexpr int ROWB = 2 * D;        // bytes per Q / dO / K row
-  constexpr int QTB = BQ * ROWB;     // bytes per Q (or dO) tile
-  constexpr int RSB = 1024 * NW;     // row-statistics area per stage (one 1 KiB copy per wave)
+  constexpr int NW = 8;
+  constexpr int BKV = 128;
+  constexpr int ROWB = 2 * D;
+  constexpr int QTB = BQ * ROWB;
+  constexpr int RSB = 2048;          // row statistics of a tile: -LSE/scale, -D (1 KiB each)
   constexpr int STAGEB = 2 * QTB + RSB;
   constexpr int NSTG = 3;
+  constexpr int NQB = BQ / 32;
+  constexpr int PLANE = 32 * 256;    // fp32 P of one key block: 32 rows of 256 bytes
   constexpr int CH_ROW = D / 8;
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int NQB = BQ / 32;
   static_assert(QTB % (1024 * NW) == 0, "a Q tile must split into whole 1 KiB copies per wave");
-  constexpr int IPW = QTB / 1024 / NW;           // copies per wave per tensor per tile
-  constexpr int DMA_OPS = 2 * IPW + 1;           // per wave per tile (Q, dO, row stats)
-  static_assert(BQ % 32 == 0, "query tile");
+  static_assert(BQ == 64, "P exchange rows hold 64 queries");
+  constexpr int IPW = QTB / 1024 / NW;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTG * STAGEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTG * STAGEB + 4 * PLANE];
   FA_LDS uint8_t* lds = (FA_LDS uint8_t*)smem;
+  FA_LDS uint8_t* p_lds = lds + NSTG * STAGEB;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kb = wave & 3;
   const int hl = lane >> 5;
   const int l32 = lane & 31;
   const int N = a.N;
@@ -124,64 +160,65 @@ bwd_kv_kernel(BwdArgs a) {
   const int kt = logical % a.n_ktiles;
   const int64_t base = (int64_t)bh * N * D;
   const uint16_t* Qg = static_cast<const uint16_t*>(a.q) + base;
-  const uint16_t* Kg = static_cast<const uint16_t*>(a.k) + base;
-  const uint16_t* Vg = static_cast<const uint16_t*>(a.v) + base;
   const uint16_t* dOg = static_cast<const uint16_t*>(a.dout) + base;
-  const f32x2_t* statg = reinterpret_cast<const f32x2_t*>(a.dsum) + (int64_t)bh * N;
+  const float* stat_lse = a.dsum + (int64_t)bh * N;
+  const float* stat_d = a.dsum + a.plane + (int64_t)bh * N;
 
   const int k0 = kt * BKV;
-  const int key = k0 + wave * 32 + l32;  // this lane's key (S accumulator column)
-  const float c = a.scale_log2;
+  const int key = k0 + kb * 32 + l32;  // this lane's key (accumulator column)
 
-  // ---- Copies (buffer loads with an LDS destination; rows past N arrive as
-  // zeros).  Copy jj of this wave fills LDS chunk (wave*IPW + jj)*64 + lane
-  // of a tile: row p / CH_ROW, swizzled chunk.
+  // ---- Copies (rows outside [0, N) arrive as zeros).
   uint32_t dma_voff[IPW];
 #pragma unroll
   for (int jj = 0; jj < IPW; ++jj) {
     const int p = (wave * IPW + jj) * 64 + lane;
     dma_voff[jj] = (uint32_t)((p / CH_ROW) * ROWB + ((p % CH_ROW) ^ swz<D>(p / CH_ROW)) * 16);
   }
-  auto copy_rows = [&](const uint16_t* src, int r0, int nrows, FA_LDS uint8_t* dst) {
-    const int rows = r0 >= N ? 0 : min(N - r0, nrows);
-    const u32x4_t r = make_rsrc(src + (int64_t)max(r0, 0) * D, rows * ROWB);
+  auto tile_rows = [&](int r0) { return (r0 < 0 || r0 >= N) ? 0 : min(N - r0, BQ); };
+  auto copy_rows = [&](const uint16_t* src, int r0, FA_LDS uint8_t* dst) {
+    const u32x4_t r = make_rsrc(src + (int64_t)max(r0, 0) * D, tile_rows(r0) * ROWB);
 #pragma unroll
     for (int jj = 0; jj < IPW; ++jj) dma16_buf(r, dma_voff[jj], dst + (wave * IPW + jj) * 1024);
   };
-  // Query tile i into stage st: Q, dO, and the row statistics of the rows
-  // [BQ/NW * wave, +BQ/NW) into this wave's 1 KiB block of the stage.
   auto issue_tile = [&](int i, int st) {
     FA_LDS uint8_t* sb = lds + st * STAGEB;
     const int q0 = i * BQ;
-    copy_rows(Qg, q0, BQ, sb);
-    copy_rows(dOg, q0, BQ, sb + QTB);
-    constexpr int RPW = BQ / NW;
-    const int r0 = q0 + wave * RPW;
-    const int rows = r0 >= N ? 0 : min(N - r0, RPW);
-    const u32x4_t r = make_rsrc(statg + max(r0, 0), rows * 8);
-    dma16_buf(r, (uint32_t)lane * 16, sb + 2 * QTB + wave * 1024);
+    copy_rows(Qg, q0, sb);
+    copy_rows(dOg, q0, sb + QTB);
+    if (wave < 2) {  // wave 0: -LSE/scale, wave 1: -D (64 rows = 256 bytes)
+      const u32x4_t r = make_rsrc((wave == 0 ? stat_lse : stat_d) + max(q0, 0), tile_rows(q0) * 4);
+      dma16_buf(r, (uint32_t)lane * 16, sb + 2 * QTB + wave * 1024);
+    }
   };
-  // Row statistics of query row q of the tile in stage sb: 4 consecutive rows
-  // (q % 4 == 0) as {-LSE/scale, -D, -LSE/scale, -D, ...}.
-  auto ld_stat4 = [&](const FA_LDS uint8_t* sb, int q, f32x4_t& lo, f32x4_t& hi) {
-    constexpr int RPW = BQ / NW;
-    const FA_LDS uint8_t* p = sb + 2 * QTB + (q / RPW) * 1024 + (q % RPW) * 8;
-    lo = *(const FA_LDS f32x4_t*)p;
-    hi = *(const FA_LDS f32x4_t*)(p + 16);
+  // Copies issued per tile: 2 IPW, plus one statistics copy for waves 0, 1.
+  auto first_tile_sync = [&]() {
+    if (wave < 2)
+      dma_sync<2 * IPW + 1>();
+    else
+      dma_sync<2 * IPW>();
+  };
+  // Mid-tile: every copy issued so far (those of the next tile) has landed
+  // and this wave's LDS writes are visible to the workgroup.
+  auto mid_sync = [&]() {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt, expcnt untouched
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  auto end_sync = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
-  // ---- LDS read offsets within a Q / dO tile (or the staged K tile).
-  // Row reads (A operand, rows = queries): row qb*32 + l32, chunk 2*dc + hl.
+  // LDS read offsets within a Q / dO tile (rows, and transposed reads).
   int roff[NDC];
   {
     const int f = swz<D>(l32);
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc) roff[dc] = l32 * ROWB + 16 * ((2 * dc + hl) ^ f);
   }
-  // Transposed reads (A operand with rows = head dims, or B operand with
-  // columns = head dims; K slots = 16 consecutive rows of the tile): supplier
-  // lane 4e + c4 of each 16-lane group addresses row 16*cc + 4*hl + e (+8) and
-  // column group 16*g2 + 4*c4 of head-dim block db.
   int toff[NDB][2];
   {
     const int e = (lane & 15) >> 2, c4 = lane & 3, g2 = (lane >> 4) & 1;
@@ -203,171 +240,198 @@ bwd_kv_kernel(BwdArgs a) {
     const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
     return __builtin_bit_cast(v8, u32x4_t{l2[0], l2[1], h2[0], h2[1]});
   };
-  // ---- Stationary operands.  K and V rows of this lane's key as B operands
-  // of S and dP (head-dim slots dc*16 + 8*hl + [0, 8)).
-  v8 kf[NDC], vf[NDC];
-#pragma unroll
-  for (int dc = 0; dc < NDC; ++dc) {
-    u32x4_t rk = {0u, 0u, 0u, 0u}, rv = {0u, 0u, 0u, 0u};
-    if (key < N) {
-      rk = ld_global16(Kg + (int64_t)key * D + dc * 16 + 8 * hl);
-      rv = ld_global16(Vg + (int64_t)key * D + dc * 16 + 8 * hl);
-    }
-    kf[dc] = __builtin_bit_cast(v8, rk);
-    vf[dc] = __builtin_bit_cast(v8, rv);
-  }
-  f32x16_t dvacc[NDB], dkacc[NDB];
-#pragma unroll
-  for (int i = 0; i < NDB; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dvacc[i][r] = 0.f;
-      dkacc[i][r] = 0.f;
-    }
+  // P exchange: the lanes of a key block form 32 rows of 256 bytes (row l32,
+  // 16-byte chunk 2 m + hl for chunk m = registers 4(m%4)..+3 of query block
+  // m/4), XOR-swizzled like the row reads of a Q tile.
+  FA_LDS uint8_t* prow = p_lds + kb * PLANE + l32 * 256;
+  const int pswz = swz<128>(l32);
+  auto pchunk = [&](int m) { return prow + 16 * ((2 * m + hl) ^ pswz); };
 
   const int nq = (N + BQ - 1) / BQ;
   const int i0 = CAUSAL ? k0 / BQ : 0;
-  // Causal: query tile i needs the mask while some of its queries precede
-  // some key of the tile.
   const int i_unmask = CAUSAL ? min(nq, (k0 + BKV + BQ - 2) / BQ) : i0;
-  uint32_t pw[NQB][2][4], dw[NQB][2][4];  // P and dS packed as B operands (chunk c of block qb)
 
-  // One query tile; MASKED applies the causal mask.
-  auto iteration = [&](auto m_tag, int i, int st) {
-    constexpr bool MASKED = decltype(m_tag)::value;
-    const FA_LDS uint8_t* sb = lds + st * STAGEB;
-    const FA_LDS uint8_t* qs = sb;
-    const FA_LDS uint8_t* os = sb + QTB;
-    const int q0 = i * BQ;
-
-    // A: S - LSE/scale and dP - D for every query block (keys as accumulator
-    // columns).  Register r of block qb is query row qb*32 + 8*(r/4) + 4*hl +
-    // r%4; the accumulators start from that row's statistics.
-    f32x16_t sacc[NQB], dpacc[NQB];
+  auto run = [&](auto role_tag) {
+    constexpr int ROLE = decltype(role_tag)::value;
+    // Stationary operand: K rows (role 0) or V rows (role 1) of this lane's
+    // key as B operands (head-dim slots dc*16 + 8*hl + [0, 8)).
+    v8 kvf[NDC];
     {
+      const uint16_t* src = static_cast<const uint16_t*>(ROLE == 0 ? a.k : a.v) + base;
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) {
+        u32x4_t rk = {0u, 0u, 0u, 0u};
+        if (key < N) rk = ld_global16(src + (int64_t)key * D + dc * 16 + 8 * hl);
+        kvf[dc] = __builtin_bit_cast(v8, rk);
+      }
+    }
+    // Completing these loads before the first copy is issued tells the
+    // compiler that no load of its own is outstanding inside the loop;
+    // otherwise it waits there for every copy in flight.
+    wait_vmcnt<0>();
+    f32x16_t acc[NDB];  // dV^T (role 0) or dK^T / scale (role 1)
+#pragma unroll
+    for (int i = 0; i < NDB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+    // P (role 0) or dS' of the previous tile (role 1) packed as B operands:
+    // pw[qb][h] covers queries qb*32 + 16 h + [0, 16).
+    uint32_t pw[NQB][2][4];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) pw[qb][h][t] = 0u;
+
+    // acc += T^T W over the 64 queries of a tile: T = dO (role 0) or Q
+    // (role 1) read transposed, W = pw; 16 queries per instruction.
+    auto acc_products = [&](const FA_LDS uint8_t* src) {
+      constexpr int PF = FA_KV2_PF_TR, NST = NDB * (BQ / 16);
+      v8 fr[PF + 1];
+#pragma unroll
+      for (int s = 0; s < PF; ++s) fr[s] = ld_tr(src, s / NDB, s % NDB);
+#pragma unroll
+      for (int s = 0; s < NST; ++s) {
+        if (s + PF < NST) fr[(s + PF) % (PF + 1)] = ld_tr(src, (s + PF) / NDB, (s + PF) % NDB);
+        const int cc = s / NDB, db = s % NDB;
+        const uint32_t* w = pw[cc >> 1][cc & 1];
+        acc[db] = E::mfma(fr[s % (PF + 1)], __builtin_bit_cast(v8, u32x4_t{w[0], w[1], w[2], w[3]}),
+                          acc[db]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    // sacc = S - LSE/scale (role 0) or dP - D (role 1) of the current tile;
+    // register r of block qb is query row qb*32 + 8*(r/4) + 4*hl + r%4.  It
+    // starts from the row statistics, loaded one tile ahead.
+    f32x16_t sacc[NQB];
+    auto load_stats = [&](int st) {
+      const FA_LDS uint8_t* ps = lds + st * STAGEB + 2 * QTB + ROLE * 1024 + 16 * hl;
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          f32x4_t st_lo, st_hi;
-          ld_stat4(sb, qb * 32 + 8 * g + 4 * hl, st_lo, st_hi);
+          const f32x4_t v = *(const FA_LDS f32x4_t*)(ps + (qb * 32 + 8 * g) * 4);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            sacc[qb][4 * g + t] = t < 2 ? st_lo[2 * t] : st_hi[2 * (t - 2)];
-            dpacc[qb][4 * g + t] = t < 2 ? st_lo[2 * t + 1] : st_hi[2 * (t - 2) + 1];
+          for (int t = 0; t < 4; ++t) sacc[qb][4 * g + t] = v[t];
+        }
+    };
+
+    auto iteration = [&](auto m_tag, int i, int st, int sp, int sn) {
+      constexpr bool MASKED = decltype(m_tag)::value;
+      const FA_LDS uint8_t* sb = lds + st * STAGEB;
+      const int q0 = i * BQ;
+
+      // Phase 1.
+      {
+        const FA_LDS uint8_t* src = sb + (ROLE == 0 ? 0 : QTB);
+        constexpr int PF = FA_KV2_PF_ROW, NST = NQB * NDC;
+        v8 fr[PF + 1];
+#pragma unroll
+        for (int s = 0; s < PF; ++s) fr[s] = ld_row(src, s / NDC, s % NDC);
+#pragma unroll
+        for (int s = 0; s < NST; ++s) {
+          if (s + PF < NST) fr[(s + PF) % (PF + 1)] = ld_row(src, (s + PF) / NDC, (s + PF) % NDC);
+          sacc[s / NDC] = E::mfma(fr[s % (PF + 1)], kvf[s % NDC], sacc[s / NDC]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if constexpr (ROLE == 0) {
+        const float c = a.scale_log2;
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            f32x4_t p4;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              float pv = fast_exp2(sacc[qb][4 * g + t] * c);
+              if constexpr (MASKED) {
+                if (key > q0 + qb * 32 + 8 * g + 4 * hl + t) pv = 0.f;
+              }
+              p4[t] = pv;
+            }
+            *(FA_LDS f32x4_t*)pchunk(qb * 4 + g) = p4;
+            pw[qb][g >> 1][2 * (g & 1)] = E::pack2(p4[0], p4[1]);
+            pw[qb][g >> 1][2 * (g & 1) + 1] = E::pack2(p4[2], p4[3]);
           }
+      } else {
+        acc_products(lds + sp * STAGEB);  // dK^T += Q(i-1)^T dS'(i-1)
+      }
+      mid_sync();
+      issue_tile(i + 2, sp);  // the stage of tile i-1, now read by every wave
+
+      // Phase 2.
+      if constexpr (ROLE == 0) {
+        acc_products(sb + QTB);  // dV^T += dO(i)^T P(i)
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4_t p4 = *(const FA_LDS f32x4_t*)pchunk(qb * 4 + g);
+            float ds[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) ds[t] = p4[t] * sacc[qb][4 * g + t];
+            pw[qb][g >> 1][2 * (g & 1)] = E::pack2(ds[0], ds[1]);
+            pw[qb][g >> 1][2 * (g & 1) + 1] = E::pack2(ds[2], ds[3]);
+          }
+      }
+      load_stats(sn);  // tile i+1 landed before the mid-tile barrier
+      // Orders this tile's P reads before the next tile's P writes.
+      end_sync();
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+
+    if (i0 < nq) {
+      // Stage 2 starts as an all-zero "tile i0-1" for the first deferred dK
+      // products (zero dS' against zero Q).
+      issue_tile(i0 - 1, 2);
+      issue_tile(i0, 0);
+      issue_tile(i0 + 1, 1);
+      first_tile_sync();
+      load_stats(0);
+      int st = 0, sp = 2, i = i0;
+      for (; i < i_unmask; ++i) {
+        const int sn = st == 2 ? 0 : st + 1;
+        iteration(T_{}, i, st, sp, sn);
+        sp = st;
+        st = sn;
+      }
+      for (; i < nq; ++i) {
+        const int sn = st == 2 ? 0 : st + 1;
+        iteration(F_{}, i, st, sp, sn);
+        sp = st;
+        st = sn;
+      }
+      if constexpr (ROLE == 1) acc_products(lds + sp * STAGEB);  // dK of the last tile
+    }
+    wait_vmcnt<0>();  // copies past the last tile must land before LDS is released
+
+    // dV (role 0) or dK = scale * dS'^T Q (role 1) for this lane's key:
+    // register r of head-dim block db is head dim db*32 + 8*(r/4) + 4*hl + r%4.
+    if (key < N) {
+      uint16_t* row = static_cast<uint16_t*>(ROLE == 0 ? a.dv : a.dk) + base + (int64_t)key * D;
+      const float f = ROLE == 0 ? 1.0f : a.scale;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2_t w;
+          w[0] = E::pack2(acc[db][4 * g + 0] * f, acc[db][4 * g + 1] * f);
+          w[1] = E::pack2(acc[db][4 * g + 2] * f, acc[db][4 * g + 3] * f);
+          *reinterpret_cast<u32x2_t*>(row + db * 32 + 8 * g + 4 * hl) = w;
         }
-      constexpr int PF = 2, NST = NQB * NDC;
-      v8 qr[PF + 1], orr[PF + 1];
-      auto load = [&](int s) {
-        qr[s % (PF + 1)] = ld_row(qs, s / NDC, s % NDC);
-        orr[s % (PF + 1)] = ld_row(os, s / NDC, s % NDC);
-      };
-#pragma unroll
-      for (int s = 0; s < PF; ++s) load(s);
-#pragma unroll
-      for (int s = 0; s < NST; ++s) {
-        if (s + PF < NST) load(s + PF);
-        const int qb = s / NDC, dc = s % NDC;
-        sacc[qb] = E::mfma(qr[s % (PF + 1)], kf[dc], sacc[qb]);
-        dpacc[qb] = E::mfma(orr[s % (PF + 1)], vf[dc], dpacc[qb]);
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
-
-    // V: probabilities and dS' of this tile, fp32, packed as B operands.
-#pragma unroll
-    for (int vg = 0; vg < NQB * 4; ++vg) {
-      const int qb = vg / 4, g = vg % 4;
-      const int qo = qb * 32 + 8 * g + 4 * hl;  // first of this lane's 4 query rows
-      float p[4], ds[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int r = 4 * g + t;
-        float pv = fast_exp2(sacc[qb][r] * c);
-        if constexpr (MASKED) {
-          if (key > q0 + qo + t) pv = 0.f;
-        }
-        p[t] = pv;
-        ds[t] = pv * dpacc[qb][r];
-      }
-      // Registers 4g..4g+3 are B-operand words (g%2)*2, +1 of chunk g/2.
-      pw[qb][g >> 1][2 * (g & 1)] = E::pack2(p[0], p[1]);
-      pw[qb][g >> 1][2 * (g & 1) + 1] = E::pack2(p[2], p[3]);
-      dw[qb][g >> 1][2 * (g & 1)] = E::pack2(ds[0], ds[1]);
-      dw[qb][g >> 1][2 * (g & 1) + 1] = E::pack2(ds[2], ds[3]);
-    }
-
-    // Refill: tile i+2 into the stage last read in the previous iteration.
-    issue_tile(i + 2, st == 0 ? 2 : st - 1);
-
-    {
-      // B: dV^T += dO^T P and dK^T += Q^T dS, 16 queries per instruction.
-      constexpr int PF = 2, NST = NDB * (BQ / 16);
-      v8 otr[PF + 1], qtr[PF + 1];
-      auto load = [&](int s) {
-        otr[s % (PF + 1)] = ld_tr(os, s / NDB, s % NDB);
-        qtr[s % (PF + 1)] = ld_tr(qs, s / NDB, s % NDB);
-      };
-#pragma unroll
-      for (int s = 0; s < PF; ++s) load(s);
-#pragma unroll
-      for (int s = 0; s < NST; ++s) {
-        if (s + PF < NST) load(s + PF);
-        const int cc = s / NDB, db = s % NDB;  // chunk cc = query block cc/2, half cc%2
-        const v8 pf = __builtin_bit_cast(v8, u32x4_t{pw[cc >> 1][cc & 1][0], pw[cc >> 1][cc & 1][1],
-                                                     pw[cc >> 1][cc & 1][2], pw[cc >> 1][cc & 1][3]});
-        const v8 df = __builtin_bit_cast(v8, u32x4_t{dw[cc >> 1][cc & 1][0], dw[cc >> 1][cc & 1][1],
-                                                     dw[cc >> 1][cc & 1][2], dw[cc >> 1][cc & 1][3]});
-        dvacc[db] = E::mfma(otr[s % (PF + 1)], pf, dvacc[db]);
-        dkacc[db] = E::mfma(qtr[s % (PF + 1)], df, dkacc[db]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // Tile i+1 must have landed; this iteration's copies may stay in flight.
-    dma_sync<DMA_OPS>();
   };
-  using T_ = std::true_type;
-  using F_ = std::false_type;
-
-  if (i0 < nq) {
-    issue_tile(i0, 0);
-    issue_tile(i0 + 1, 1);
-    dma_sync<DMA_OPS>();
-    int st = 0, i = i0;
-    for (; i < i_unmask; ++i) {
-      iteration(T_{}, i, st);
-      st = st == 2 ? 0 : st + 1;
-    }
-    for (; i < nq; ++i) {
-      iteration(F_{}, i, st);
-      st = st == 2 ? 0 : st + 1;
-    }
-  }
-  wait_vmcnt<0>();  // copies past the last tile must land before LDS is released
-
-  // dK = scale * dS'^T Q and dV for this lane's key: register r
-  // of head-dim block db is head dim db*32 + 8*(r/4) + 4*hl + r%4.
-  if (key < N) {
-    uint16_t* dkrow = static_cast<uint16_t*>(a.dk) + base + (int64_t)key * D;
-    uint16_t* dvrow = static_cast<uint16_t*>(a.dv) + base + (int64_t)key * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = db * 32 + 8 * g + 4 * hl;
-        u32x2_t w;
-        w[0] = E::pack2(dkacc[db][4 * g + 0] * a.scale, dkacc[db][4 * g + 1] * a.scale);
-        w[1] = E::pack2(dkacc[db][4 * g + 2] * a.scale, dkacc[db][4 * g + 3] * a.scale);
-        *reinterpret_cast<u32x2_t*>(dkrow + d0) = w;
-        w[0] = E::pack2(dvacc[db][4 * g + 0], dvacc[db][4 * g + 1]);
-        w[1] = E::pack2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]);
-        *reinterpret_cast<u32x2_t*>(dvrow + d0) = w;
-      }
-    }
-  }
+  if (wave < 4)
+    run(std::integral_constant<int, 0>{});
+  else
+    run(std::integral_constant<int, 1>{});
 }
-
 
 // dQ by recomputation, query-stationary: one workgroup per (b, h, tile of
 // BM = 32*NW queries), wave w owns queries [32 w, 32 w + 32).  Like the
@@ -418,7 +482,8 @@ bwd_dq_kernel(BwdArgs a) {
   const uint16_t* Kg = static_cast<const uint16_t*>(a.k) + base;
   const uint16_t* Vg = static_cast<const uint16_t*>(a.v) + base;
   const uint16_t* dOg = static_cast<const uint16_t*>(a.dout) + base;
-  const f32x2_t* statg = reinterpret_cast<const f32x2_t*>(a.dsum) + (int64_t)bh * N;
+  const float* stat_lse = a.dsum + (int64_t)bh * N;
+  const float* stat_d = a.dsum + a.plane + (int64_t)bh * N;
 
   const int q0 = qt * BM;
   const int qw0 = q0 + wave * 32;
@@ -459,7 +524,7 @@ bwd_dq_kernel(BwdArgs a) {
     of[dc] = __builtin_bit_cast(v8, ro);
   }
   f32x2_t stat = {0.f, 0.f};
-  if (qrow < N) stat = statg[qrow];  // (-LSE/scale, -D)
+  if (qrow < N) stat = f32x2_t{stat_lse[qrow], stat_d[qrow]};  // (-LSE/scale, -D)
   const float pbias = stat[0] * c;    // -LSE * log2 e
 
   f32x16_t dqacc[NDB];
@@ -530,6 +595,9 @@ bwd_dq_kernel(BwdArgs a) {
         const int kb = s / NDC, dc = s % NDC;
         sacc[kb] = E::mfma(kr[s % (PF + 1)], qf[dc], sacc[kb]);
         dpacc[kb] = E::mfma(vr[s % (PF + 1)], of[dc], dpacc[kb]);
+        // Two waves share each SIMD: hand the issue lead over within a tile.
+        if (s == 0) __builtin_amdgcn_s_setprio(1);
+        if (s == NST - 1) __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -613,19 +681,19 @@ hipError_t launch_d(const BwdArgs& a0, int BH, bool causal, hipStream_t s) {
   if (pre_blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((bwd_pre_kernel<D, DT>), dim3((unsigned)pre_blocks), dim3(256), 0, s,
                      static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout),
-                     a.lse, reinterpret_cast<f32x2_t*>(a.dsum), rows, 1.0f / a.scale);
+                     a.lse, a.dsum, rows, 1.0f / a.scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int BKV = 32 * NW;
+  a.plane = rows;
+  constexpr int BKV = 128;
   a.n_ktiles = (a.N + BKV - 1) / BKV;
   int64_t grid = (int64_t)a.n_ktiles * BH;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (causal)
-    hipLaunchKernelGGL((bwd_kv_kernel<D, NW, BQ, true, DT>), dim3((unsigned)grid), dim3(NW * 64),
-                       0, s, a);
+    hipLaunchKernelGGL((bwd_kv2_kernel<D, BQ, true, DT>), dim3((unsigned)grid), dim3(512), 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_kv_kernel<D, NW, BQ, false, DT>), dim3((unsigned)grid),
-                       dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((bwd_kv2_kernel<D, BQ, false, DT>), dim3((unsigned)grid), dim3(512), 0, s, a);
+
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int BM = 32 * DQ_NW;

@@ -29,7 +29,8 @@ struct BwdArgs {
   const void* o;
   const void* dout;
   const float* lse;
-  float* dsum;       // workspace: [B][H][N] pairs (LSE * log2 e, rowsum(dO o O))
+  float* dsum;       // workspace: two planes of B*H*N floats, -LSE/scale then -rowsum(dO o O)
+  int64_t plane;     // B*H*N, filled in by the launcher
   float* dq;         // fp32 [B][H][N][d], zeroed by the preprocess kernel
   void* dk;
   void* dv;
