@@ -27,6 +27,9 @@
 //     exp2 reference raised lazily; probabilities rounded to the input type;
 //   O^T += V_j^T P^T on matrix cores, V read from LDS by transposed 16-bit
 //     reads; O^T has one query per lane, so the rescale is a per-lane multiply.
+#include <algorithm>
+#include <atomic>
+#include <cstdlib>
 #include <type_traits>
 
 #include "common.h"
@@ -55,7 +58,49 @@ __device__ __forceinline__ int swz(int r) {
 // QB = query blocks of 32 rows per wave; OCC = waves per SIMD the register
 // budget is sized for (1: 512 registers, 2: 256); NSTG = LDS stages per
 // tensor (2 or 3, see the pipeline description below).
-template <int D, int BN, int NW, int QB, int OCC, int NSTG, bool CAUSAL, int DT>
+// Persistent causal schedule.  A causal query tile qt costs qt + 1 key
+// tiles, so the units are taken heaviest first (longest-processing-time
+// order): unit k of a list holds query tile n_qtiles - 1 - k / heads of head
+// k % heads.  The grid's G workgroups take the list in rounds of G, in
+// alternating direction (round r: workgroup w takes unit r G + w when r is
+// even, r G + G - 1 - w when odd), so that each workgroup's heavy and light
+// units pair up and every workgroup ends with nearly the same total.  When
+// the heads and the grid both split evenly over the 8 XCDs (a.pin), each XCD
+// keeps its own heads (head x + 8 i on XCD x, which runs workgroups w with
+// w % 8 == x) so that a head's K and V stay in one L2.
+template <typename F>
+__device__ __forceinline__ void persistent_units(const FwdArgs& a, F&& run) {
+  constexpr int kXcd = 8;
+  const int w = blockIdx.x;
+  const int G = gridDim.x;
+  const int nq = a.n_qtiles;
+  int v, g, heads, x;
+  if (a.pin) {
+    x = w % kXcd;
+    v = w / kXcd;
+    g = G / kXcd;
+    heads = a.bh / kXcd;
+  } else {
+    x = 0;
+    v = w;
+    g = G;
+    heads = a.bh;
+  }
+  const int units = heads * nq;
+  for (int r = 0; r * g < units; ++r) {
+    const int k = r * g + ((r & 1) ? g - 1 - v : v);
+    if (k < units) {
+      const int qt = nq - 1 - k / heads;
+      const int hi = k % heads;
+      run(a.pin ? x + kXcd * hi : hi, qt);
+    }
+  }
+}
+
+// PERSIST: the grid holds one workgroup per resident slot, and each loops
+// over the work units (b, h, query tile) of a fixed causal schedule (see
+// persistent_units below); otherwise each workgroup takes one unit.
+template <int D, int BN, int NW, int QB, int OCC, int NSTG, bool CAUSAL, int DT, bool PERSIST>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 fwd_kernel(FwdArgs a) {
   using E = Elem<DT>;
@@ -76,17 +121,19 @@ fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NSTG * TILEB];
   FA_LDS uint8_t* lds = (FA_LDS uint8_t*)smem;  // K stage s at s*TILEB, V at (NSTG+s)*TILEB
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
-  const int hl = lane >> 5;  // which half of K slots / accumulator rows
-  const int l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave-uniform (scalar)
   const int N = a.N;
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / a.n_qtiles;
-  int qt = logical % a.n_qtiles;
-  if (CAUSAL) qt = a.n_qtiles - 1 - qt;  // longest key ranges first
+  // One work unit: query tile qt of head bh.
+  auto unit = [&](const int bh, const int qt) {
+  // The lane index passes through an empty asm so that nothing derived from
+  // it is hoisted out of a loop over units (it would stay live across units
+  // and spill at the register limit).
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int hl = lane >> 5;  // which half of K slots / accumulator rows
+  const int l32 = lane & 31;
   const int64_t base = (int64_t)bh * N * D;
   const uint16_t* Q = static_cast<const uint16_t*>(a.q) + base;
   const uint16_t* K = static_cast<const uint16_t*>(a.k) + base;
@@ -447,6 +494,23 @@ fwd_kernel(FwdArgs a) {
         a.lse[(int64_t)bh * N + qrow] = m_run[qb] * kLn2 + __logf(l_tot);
     }
   }
+  };  // unit
+
+  if constexpr (PERSIST) {
+    persistent_units(a, [&](int bh, int qt) {
+      unit(bh, qt);
+      // The next unit's first copies reuse the ring: every wave must be done
+      // reading it (this wave's own copies have all landed already).
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    });
+  } else {
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = logical / a.n_qtiles;
+    int qt = logical % a.n_qtiles;
+    if (CAUSAL) qt = a.n_qtiles - 1 - qt;  // longest key ranges first
+    unit(bh, qt);
+  }
 }
 
 // Per head dimension: keys per tile, waves per workgroup, query blocks per
@@ -470,22 +534,55 @@ template <> struct FwdCfg<128> { static constexpr int BN = 64, NW = 8, QB = 1, O
 #endif
 template <> struct FwdCfg<256> { static constexpr int BN = 32, NW = 4, QB = 1, OCC = 1, NSTG = 3; };
 
-template <int D, bool CAUSAL, int DT>
+// Workgroups of `kernel` resident at once on the current device.
+template <typename K>
+int query_resident_slots(K kernel, int threads) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
+  return cus * per_cu;
+}
+
+template <int D, bool CAUSAL, bool PERSIST, int DT>
 hipError_t launch_one(const FwdArgs& a, int BH, hipStream_t stream) {
   using C = FwdCfg<D>;
   constexpr int BM = 32 * C::QB * C::NW;
   FwdArgs args = a;
   args.n_qtiles = (a.N + BM - 1) / BM;
-  const int64_t grid = (int64_t)args.n_qtiles * BH;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_kernel<D, C::BN, C::NW, C::QB, C::OCC, C::NSTG, CAUSAL, DT>), dim3((unsigned)grid),
-                     dim3(C::NW * 64), 0, stream, args);
+  args.bh = BH;
+  const int64_t units = (int64_t)args.n_qtiles * BH;
+  if (units > 0x7fffffff) return hipErrorInvalidValue;
+  auto kernel = fwd_kernel<D, C::BN, C::NW, C::QB, C::OCC, C::NSTG, CAUSAL, DT, PERSIST>;
+  int64_t grid = units;
+  if constexpr (PERSIST) {
+    // Device property cache, filled once per device and instantiation.
+    constexpr int kMaxDev = 16;
+    static std::atomic<int> cache[kMaxDev];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidValue;
+    int slots = dev < kMaxDev ? cache[dev].load(std::memory_order_relaxed) : 0;
+    if (slots <= 0) {
+      slots = query_resident_slots(kernel, C::NW * 64);
+      if (dev < kMaxDev) cache[dev].store(slots, std::memory_order_relaxed);
+    }
+    if (slots <= 0) return hipErrorInvalidValue;
+    grid = std::min<int64_t>(units, slots);
+    args.pin = (BH % 8 == 0 && grid % 8 == 0) ? 1 : 0;
+  }
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(C::NW * 64), 0, stream, args);
   return hipGetLastError();
 }
 
+// Causal schedule: FA_FWD_SCHED=1 gives one workgroup per query tile in
+// dispatch order (heaviest tile of each head first), anything else the
+// persistent schedule.
 template <int D, int DT>
 hipError_t launch_causal(const FwdArgs& a, int BH, bool causal, hipStream_t s) {
-  return causal ? launch_one<D, true, DT>(a, BH, s) : launch_one<D, false, DT>(a, BH, s);
+  if (!causal) return launch_one<D, false, false, DT>(a, BH, s);
+  const char* e = std::getenv("FA_FWD_SCHED");
+  if (e != nullptr && std::atoi(e) == 1) return launch_one<D, true, false, DT>(a, BH, s);
+  return launch_one<D, true, true, DT>(a, BH, s);
 }
 
 template <int DT>

@@ -16,6 +16,8 @@ struct FwdArgs {
   int N;
   int n_qtiles;      // filled in by the launcher
   float scale_log2;  // softmax scale * log2(e)
+  int bh;            // B * H (launcher)
+  int pin;           // persistent schedule keeps each head on one XCD (launcher)
 };
 
 // Enqueue the 16-bit forward.  Arguments are validated by the caller.

@@ -194,3 +194,39 @@ def test_two_streams_concurrently():
     assert torch.equal(outs[0], ref)
     o_ref, _ = attention_fwd(q64[:1, :2], k64[:1, :2], v64[:1, :2], causal=False)
     assert max_abs(outs[1][:1, :2].double().cpu().numpy(), o_ref) <= O_MAX_ABS
+
+
+# ------------------------------------------------------------ causal schedule
+
+@pytest.mark.parametrize("B,H,N,d", [(2, 16, 8192, 128),   # heads pinned to XCDs, 4 rounds
+                                     (3, 7, 4096, 128),    # 21 heads: unpinned, 2 rounds
+                                     (1, 5, 3000, 64),     # ragged, one partial round
+                                     (2, 9, 2048, 256)])   # 128-row tiles, 18 heads
+def test_causal_schedules_agree(B, H, N, d, monkeypatch):
+    """The persistent heaviest-first causal schedule (the default) and one
+    workgroup per query tile (FA_FWD_SCHED=1) run the same per-tile
+    arithmetic, so they must agree bit for bit; every output element must be
+    written (outputs start as NaN); sampled rows of the first and last heads
+    match the oracle."""
+    import torch
+    fa = _fa()
+    _banner(f"causal schedules B={B} H={H} N={N} d={d}")
+    (qt, kt, vt), (q64, k64, v64) = _case(B, H, N, d, 60 + d, "bf16")
+    q, k, v = to_device(qt), to_device(kt), to_device(vt)
+    res = []
+    for sched in ("0", "1"):
+        monkeypatch.setenv("FA_FWD_SCHED", sched)
+        o = torch.full((B, H, N, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
+        fa.fwd(q, k, v, causal=True, out=o, lse=lse)
+        torch.cuda.synchronize()
+        assert not torch.isnan(o).any() and not torch.isnan(lse).any(), sched
+        res.append((o, lse))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+    o = res[0][0].to(torch.float64).cpu().numpy()
+    lse = res[0][1].to(torch.float64).cpu().numpy()
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        rows = sample_rows(N, seed=7 * b + h)
+        o_ref, lse_ref = attention_fwd_rows(q64[b, h], k64[b, h], v64[b, h], rows, causal=True)
+        assert max_abs(o[b, h, rows], o_ref) <= O_MAX_ABS, (b, h)
+        assert max_abs(lse[b, h, rows], lse_ref) <= LSE_MAX_ABS, (b, h)
