@@ -22,7 +22,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
 ARCH = "gfx950"
-SOURCES = ["fa_api.cpp", "fwd.hip", "bwd.hip", "quant.hip", "fwd_fp8.hip"]
+SOURCES = ["fa_api.cpp", "fwd.hip", "bwd.hip", "quant.hip", "fwd_fp8.hip", "merge.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

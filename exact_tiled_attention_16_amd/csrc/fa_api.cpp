@@ -21,6 +21,10 @@ bool valid_dims(int B, int H, int N) {
 
 bool supported_d(int d) { return d == 64 || d == 128 || d == 256; }
 
+// Longest sequence and largest position of the split-KV calls (keeps the
+// kernels' 32-bit position arithmetic far from overflow).
+constexpr int kMaxLen = 1 << 29;
+
 bool valid_scale(float s) { return isfinite(s) && s > 0.f; }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
@@ -59,6 +63,102 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
       fa::launch_fwd(a, B, H, d, dtype, causal != 0, static_cast<hipStream_t>(stream)));
 }
 
+
+int fa_fwd_partial(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                   int H, int Nq, int Nk, int d, int dtype, float scale, int causal, int q_pos0,
+                   int k_pos0, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
+    return FA_ERR_INVALID;
+  if (!valid_dims(B, H, Nq) || !valid_dims(B, H, Nk)) return FA_ERR_INVALID;
+  if (Nq > kMaxLen || Nk > kMaxLen || (dtype != FA_BF16 && dtype != FA_FP16))
+    return FA_ERR_INVALID;
+  if (q_pos0 < 0 || k_pos0 < 0 || q_pos0 > kMaxLen || k_pos0 > kMaxLen) return FA_ERR_INVALID;
+  if (!valid_scale(scale) || (causal != 0 && causal != 1)) return FA_ERR_INVALID;
+  if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+  fa::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.N = Nq;
+  a.Nk = Nk;
+  a.c_off = q_pos0 - k_pos0;
+  a.k_chunk = Nk;
+  a.n_split = 1;
+  a.o32 = o;
+  a.lse32 = lse;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return launch_status(
+      fa::launch_fwd_partial(a, B, H, d, dtype, causal != 0, static_cast<hipStream_t>(stream)));
+}
+
+int fa_merge(const float* o_parts, const float* lse_parts, int n_parts, void* o, float* lse,
+             int B, int H, int N, int d, int dtype, void* stream) {
+  if (!o_parts || !lse_parts || !o) return FA_ERR_INVALID;
+  if (!aligned16(o_parts) || !aligned4(lse_parts) || !aligned16(o) || !aligned4(lse))
+    return FA_ERR_INVALID;
+  if (!valid_dims(B, H, N) || n_parts < 1 || (dtype != FA_BF16 && dtype != FA_FP16))
+    return FA_ERR_INVALID;
+  if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+  fa::MergeArgs a{};
+  a.o_parts = o_parts;
+  a.lse_parts = lse_parts;
+  a.o = o;
+  a.lse = lse;
+  a.rows = (int64_t)B * H * N;
+  a.n_parts = n_parts;
+  return launch_status(fa::launch_merge(a, d, dtype, static_cast<hipStream_t>(stream)));
+}
+
+size_t fa_splitkv_workspace_size(int B, int H, int Nq, int d, int n_splits) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || n_splits <= 0 || !supported_d(d)) return 0;
+  const size_t rows = (size_t)B * H * Nq * n_splits;
+  return rows * (size_t)(d + 1) * sizeof(float);  // partial O, then partial LSE
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   void* workspace, int B, int H, int Nq, int Nk, int d, int dtype, float scale,
+                   int causal, int n_splits, void* stream) {
+  if (!q || !k || !v || !o || !workspace) return FA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse) ||
+      !aligned16(workspace))
+    return FA_ERR_INVALID;
+  if (!valid_dims(B, H, Nq) || !valid_dims(B, H, Nk) || n_splits < 1) return FA_ERR_INVALID;
+  if (Nq > kMaxLen || Nk > kMaxLen || (dtype != FA_BF16 && dtype != FA_FP16))
+    return FA_ERR_INVALID;
+  if (!valid_scale(scale) || (causal != 0 && causal != 1)) return FA_ERR_INVALID;
+  if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+  // Parts of a whole number of 64-key tiles; the last may be shorter.
+  const int per = (Nk + n_splits - 1) / n_splits;
+  const int chunk = (per + 63) / 64 * 64;
+  const int parts = (Nk + chunk - 1) / chunk;
+  const int64_t rows = (int64_t)B * H * Nq;
+  float* o32 = static_cast<float*>(workspace);
+  float* lse32 = o32 + rows * parts * d;
+  fa::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.N = Nq;
+  a.Nk = Nk;
+  a.c_off = Nk - Nq;
+  a.k_chunk = chunk;
+  a.n_split = parts;
+  a.o32 = o32;
+  a.lse32 = lse32;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = fa::launch_fwd_partial(a, B, H, d, dtype, causal != 0, s);
+  if (e != hipSuccess) return FA_ERR_LAUNCH;
+  fa::MergeArgs m{};
+  m.o_parts = o32;
+  m.lse_parts = lse32;
+  m.o = o;
+  m.lse = lse;
+  m.rows = rows;
+  m.n_parts = parts;
+  return launch_status(fa::launch_merge(m, d, dtype, s));
+}
 
 int fa_quant_fp8(const void* x, int dtype, void* x8, float* scales, const float* signs,
                  float scale_mul, int per_tensor, int B, int H, int N, int d, void* stream) {

@@ -100,7 +100,12 @@ __device__ __forceinline__ void persistent_units(const FwdArgs& a, F&& run) {
 // PERSIST: the grid holds one workgroup per resident slot, and each loops
 // over the work units (b, h, query tile) of a fixed causal schedule (see
 // persistent_units below); otherwise each workgroup takes one unit.
-template <int D, int BN, int NW, int QB, int OCC, int NSTG, bool CAUSAL, int DT, bool PERSIST>
+// PARTIAL: split-KV mode.  Unit (b, h, query tile, split s) attends to keys
+// [s k_chunk, (s+1) k_chunk) only and writes O normalised over those keys in
+// fp32 and their log-sum-exp to slot s of the partial outputs; a merge kernel
+// combines the slots.
+template <int D, int BN, int NW, int QB, int OCC, int NSTG, bool CAUSAL, int DT, bool PERSIST,
+          bool PARTIAL>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 fwd_kernel(FwdArgs a) {
   using E = Elem<DT>;
@@ -124,8 +129,8 @@ fwd_kernel(FwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave-uniform (scalar)
   const int N = a.N;
 
-  // One work unit: query tile qt of head bh.
-  auto unit = [&](const int bh, const int qt) {
+  // One work unit: query tile qt of head bh against the keys of split s.
+  auto unit = [&](const int bh, const int qt, const int s) {
   // The lane index passes through an empty asm so that nothing derived from
   // it is hoisted out of a loop over units (it would stay live across units
   // and spill at the register limit).
@@ -134,14 +139,20 @@ fwd_kernel(FwdArgs a) {
   const int lane = tid & 63;
   const int hl = lane >> 5;  // which half of K slots / accumulator rows
   const int l32 = lane & 31;
+  // Keys of this unit: [kb0, kb0 + kn) of the head's Nk.  Causal: query row
+  // i sees local key j iff j <= i + coff (coff = 0 for the plain forward).
+  const int kb0 = s * a.k_chunk;
+  const int kn = max(min(a.Nk - kb0, a.k_chunk), 0);
+  const int coff = a.c_off - kb0;
   const int64_t base = (int64_t)bh * N * D;
+  const int64_t kvbase = ((int64_t)bh * a.Nk + kb0) * D;
   const uint16_t* Q = static_cast<const uint16_t*>(a.q) + base;
-  const uint16_t* K = static_cast<const uint16_t*>(a.k) + base;
-  const uint16_t* V = static_cast<const uint16_t*>(a.v) + base;
+  const uint16_t* K = static_cast<const uint16_t*>(a.k) + kvbase;
+  const uint16_t* V = static_cast<const uint16_t*>(a.v) + kvbase;
 
   const int q0 = qt * BM;
   const int qw0 = q0 + wave * WQ;  // first query row of this wave
-  const int kend = CAUSAL ? min(N, q0 + BM) : N;
+  const int kend = CAUSAL ? max(min(kn, q0 + BM + coff), 0) : kn;
   const int ntiles = (kend + BN - 1) / BN;
   const float c = a.scale_log2;
 
@@ -157,7 +168,7 @@ fwd_kernel(FwdArgs a) {
     dma_voff[jj] = (uint32_t)((p / CH_ROW) * ROWB + ((p % CH_ROW) ^ swz<D>(p / CH_ROW)) * 16);
   }
   auto issue = [&](const uint16_t* src, int t, FA_LDS uint8_t* stage) {
-    const int rows = t < 0 ? 0 : min(max(N - t * BN, 0), BN);
+    const int rows = t < 0 ? 0 : min(max(kn - t * BN, 0), BN);
     const u32x4_t r = make_rsrc(src + (int64_t)t * BN * D, rows * ROWB);
 #pragma unroll
     for (int jj = 0; jj < IPW; ++jj) dma16_buf(r, dma_voff[jj], stage + (wave * IPW + jj) * 1024);
@@ -330,8 +341,8 @@ fwd_kernel(FwdArgs a) {
   // they were issued one iteration earlier and this iteration's copies stay
   // in flight; with two stages (half the LDS, so two workgroups fit on a CU)
   // they were issued at the start of this iteration and the wait drains all.
-  int t_mask = (N % BN) ? N / BN : ntiles;
-  if (CAUSAL) t_mask = min(t_mask, (q0 + 1) / BN);
+  int t_mask = (kn % BN) ? kn / BN : ntiles;
+  if (CAUSAL) t_mask = min(t_mask, max(q0 + coff + 1, 0) / BN);
   t_mask = min(t_mask, ntiles);
 
   Scores sA, sB;
@@ -417,8 +428,8 @@ fwd_kernel(FwdArgs a) {
       const int t = j + 1;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        int lim = N - t * BN - 4 * hl;
-        if (CAUSAL) lim = min(lim, qw0 + 32 * qb + l32 + 1 - t * BN - 4 * hl);
+        int lim = kn - t * BN - 4 * hl;
+        if (CAUSAL) lim = min(lim, qw0 + 32 * qb + l32 + 1 + coff - t * BN - 4 * hl);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -479,37 +490,54 @@ fwd_kernel(FwdArgs a) {
     const float l_tot = sum_halves(l_run[qb]);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow < N) {
-      uint16_t* orow = static_cast<uint16_t*>(a.o) + base + (int64_t)qrow * D;
+      if constexpr (PARTIAL) {
+        const int64_t slot = ((int64_t)s * a.bh + bh) * N + qrow;
+        float* orow = a.o32 + slot * D;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
+        for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          u32x2_t w;
-          w[0] = E::pack2(oacc[qb][db][4 * g + 0] * inv, oacc[qb][db][4 * g + 1] * inv);
-          w[1] = E::pack2(oacc[qb][db][4 * g + 2] * inv, oacc[qb][db][4 * g + 3] * inv);
-          *reinterpret_cast<u32x2_t*>(orow + db * 32 + 8 * g + 4 * hl) = w;
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<f32x4_t*>(orow + db * 32 + 8 * g + 4 * hl) =
+                f32x4_t{oacc[qb][db][4 * g + 0], oacc[qb][db][4 * g + 1], oacc[qb][db][4 * g + 2],
+                        oacc[qb][db][4 * g + 3]} * inv;
         }
+        // No visible key: l = 0, O = 0 and the log-sum-exp is -inf.
+        if (hl == 0) a.lse32[slot] = m_run[qb] * kLn2 + __logf(l_tot);
+      } else {
+        uint16_t* orow = static_cast<uint16_t*>(a.o) + base + (int64_t)qrow * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            u32x2_t w;
+            w[0] = E::pack2(oacc[qb][db][4 * g + 0] * inv, oacc[qb][db][4 * g + 1] * inv);
+            w[1] = E::pack2(oacc[qb][db][4 * g + 2] * inv, oacc[qb][db][4 * g + 3] * inv);
+            *reinterpret_cast<u32x2_t*>(orow + db * 32 + 8 * g + 4 * hl) = w;
+          }
+        }
+        if (hl == 0 && a.lse != nullptr)
+          a.lse[(int64_t)bh * N + qrow] = m_run[qb] * kLn2 + __logf(l_tot);
       }
-      if (hl == 0 && a.lse != nullptr)
-        a.lse[(int64_t)bh * N + qrow] = m_run[qb] * kLn2 + __logf(l_tot);
     }
   }
   };  // unit
 
   if constexpr (PERSIST) {
     persistent_units(a, [&](int bh, int qt) {
-      unit(bh, qt);
+      unit(bh, qt, 0);
       // The next unit's first copies reuse the ring: every wave must be done
       // reading it (this wave's own copies have all landed already).
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     });
   } else {
+    // Units in (head, split, query tile) order: the query tiles of one split
+    // read the same keys, and the XCD remap keeps them on one L2.
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = logical / a.n_qtiles;
+    const int hs = logical / a.n_qtiles;
     int qt = logical % a.n_qtiles;
     if (CAUSAL) qt = a.n_qtiles - 1 - qt;  // longest key ranges first
-    unit(bh, qt);
+    unit(hs / a.n_split, qt, hs % a.n_split);
   }
 }
 
@@ -544,16 +572,16 @@ int query_resident_slots(K kernel, int threads) {
   return cus * per_cu;
 }
 
-template <int D, bool CAUSAL, bool PERSIST, int DT>
+template <int D, bool CAUSAL, bool PERSIST, bool PARTIAL, int DT>
 hipError_t launch_one(const FwdArgs& a, int BH, hipStream_t stream) {
   using C = FwdCfg<D>;
   constexpr int BM = 32 * C::QB * C::NW;
   FwdArgs args = a;
   args.n_qtiles = (a.N + BM - 1) / BM;
   args.bh = BH;
-  const int64_t units = (int64_t)args.n_qtiles * BH;
+  const int64_t units = (int64_t)args.n_qtiles * BH * args.n_split;
   if (units > 0x7fffffff) return hipErrorInvalidValue;
-  auto kernel = fwd_kernel<D, C::BN, C::NW, C::QB, C::OCC, C::NSTG, CAUSAL, DT, PERSIST>;
+  auto kernel = fwd_kernel<D, C::BN, C::NW, C::QB, C::OCC, C::NSTG, CAUSAL, DT, PERSIST, PARTIAL>;
   int64_t grid = units;
   if constexpr (PERSIST) {
     // Device property cache, filled once per device and instantiation.
@@ -579,10 +607,10 @@ hipError_t launch_one(const FwdArgs& a, int BH, hipStream_t stream) {
 // persistent schedule.
 template <int D, int DT>
 hipError_t launch_causal(const FwdArgs& a, int BH, bool causal, hipStream_t s) {
-  if (!causal) return launch_one<D, false, false, DT>(a, BH, s);
+  if (!causal) return launch_one<D, false, false, false, DT>(a, BH, s);
   const char* e = std::getenv("FA_FWD_SCHED");
-  if (e != nullptr && std::atoi(e) == 1) return launch_one<D, true, false, DT>(a, BH, s);
-  return launch_one<D, true, true, DT>(a, BH, s);
+  if (e != nullptr && std::atoi(e) == 1) return launch_one<D, true, false, false, DT>(a, BH, s);
+  return launch_one<D, true, true, false, DT>(a, BH, s);
 }
 
 template <int DT>
@@ -595,13 +623,41 @@ hipError_t launch_dtype(const FwdArgs& a, int BH, int d, bool causal, hipStream_
   }
 }
 
+template <int D, int DT>
+hipError_t launch_partial_d(const FwdArgs& a, int BH, bool causal, hipStream_t s) {
+  return causal ? launch_one<D, true, false, true, DT>(a, BH, s)
+                : launch_one<D, false, false, true, DT>(a, BH, s);
+}
+
+template <int DT>
+hipError_t launch_partial_dtype(const FwdArgs& a, int BH, int d, bool causal, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_partial_d<64, DT>(a, BH, causal, s);
+    case 128: return launch_partial_d<128, DT>(a, BH, causal, s);
+    case 256: return launch_partial_d<256, DT>(a, BH, causal, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
-hipError_t launch_fwd(const FwdArgs& a, int B, int H, int d, int dtype, bool causal,
+hipError_t launch_fwd(const FwdArgs& a0, int B, int H, int d, int dtype, bool causal,
                       hipStream_t stream) {
+  FwdArgs a = a0;
+  a.Nk = a.N;  // every key, one split, top-left diagonal
+  a.c_off = 0;
+  a.k_chunk = a.N;
+  a.n_split = 1;
   const int BH = B * H;
   return dtype == 0 ? launch_dtype<0>(a, BH, d, causal, stream)
                     : launch_dtype<1>(a, BH, d, causal, stream);
+}
+
+hipError_t launch_fwd_partial(const FwdArgs& a, int B, int H, int d, int dtype, bool causal,
+                              hipStream_t stream) {
+  const int BH = B * H;
+  return dtype == 0 ? launch_partial_dtype<0>(a, BH, d, causal, stream)
+                    : launch_partial_dtype<1>(a, BH, d, causal, stream);
 }
 
 }  // namespace fa

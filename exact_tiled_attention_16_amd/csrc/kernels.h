@@ -8,21 +8,44 @@
 namespace fa {
 
 struct FwdArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  void* o;
-  float* lse;
-  int N;
+  const void* q;     // [B][H][N][d]
+  const void* k;     // [B][H][Nk][d]
+  const void* v;     // [B][H][Nk][d]
+  void* o;           // [B][H][N][d] (plain forward)
+  float* lse;        // [B][H][N] or null (plain forward)
+  int N;             // query rows per head
   int n_qtiles;      // filled in by the launcher
   float scale_log2;  // softmax scale * log2(e)
   int bh;            // B * H (launcher)
   int pin;           // persistent schedule keeps each head on one XCD (launcher)
+  // Split-KV (launch_fwd_partial; launch_fwd sets one split over all keys):
+  int Nk;            // key rows per head
+  int c_off;         // causal: query row i sees key j iff j <= i + c_off
+  int k_chunk;       // keys per split
+  int n_split;       // splits: split s covers keys [s k_chunk, (s+1) k_chunk)
+  float* o32;        // [n_split][B][H][N][d] fp32, O normalised within the split
+  float* lse32;      // [n_split][B][H][N], log-sum-exp within the split (-inf if empty)
 };
 
 // Enqueue the 16-bit forward.  Arguments are validated by the caller.
 hipError_t launch_fwd(const FwdArgs& a, int B, int H, int d, int dtype, bool causal,
                       hipStream_t stream);
+
+// Enqueue the split-KV partial forward (fp32 partial outputs per split).
+hipError_t launch_fwd_partial(const FwdArgs& a, int B, int H, int d, int dtype, bool causal,
+                              hipStream_t stream);
+
+struct MergeArgs {
+  const float* o_parts;    // [S][rows][d] fp32
+  const float* lse_parts;  // [S][rows]
+  void* o;                 // [rows][d], 16-bit type
+  float* lse;              // [rows] or null
+  int64_t rows;            // B * H * N
+  int n_parts;             // S
+};
+
+// Enqueue the log-sum-exp merge of S partial results.
+hipError_t launch_merge(const MergeArgs& a, int d, int dtype, hipStream_t stream);
 
 struct BwdArgs {
   const void* q;

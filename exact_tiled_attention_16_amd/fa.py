@@ -39,6 +39,12 @@ SIGNATURES = {
     "fa_bwd_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
                     _I, _F, _I, _P]),
+    "fa_fwd_partial": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
+                            _I, _I, _P]),
+    "fa_merge": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "fa_splitkv_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "fa_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F,
+                            _I, _I, _P]),
     "fa_status_str": (ctypes.c_char_p, [_I]),
 }
 
@@ -103,6 +109,28 @@ def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, B, H, N, d, dtype, scale,
            causal, stream) -> int:
     return lib().fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, B, H, N, d,
                         dtype, scale, causal, stream)
+
+
+def fa_fwd_partial(q, k, v, o, lse, B, H, Nq, Nk, d, dtype, scale, causal,
+                   q_pos0, k_pos0, stream) -> int:
+    return lib().fa_fwd_partial(q, k, v, o, lse, B, H, Nq, Nk, d, dtype, scale,
+                                causal, q_pos0, k_pos0, stream)
+
+
+def fa_merge(o_parts, lse_parts, n_parts, o, lse, B, H, N, d, dtype,
+             stream) -> int:
+    return lib().fa_merge(o_parts, lse_parts, n_parts, o, lse, B, H, N, d,
+                          dtype, stream)
+
+
+def fa_splitkv_workspace_size(B, H, Nq, d, n_splits) -> int:
+    return lib().fa_splitkv_workspace_size(B, H, Nq, d, n_splits)
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, ws, B, H, Nq, Nk, d, dtype, scale, causal,
+                   n_splits, stream) -> int:
+    return lib().fa_fwd_splitkv(q, k, v, o, lse, ws, B, H, Nq, Nk, d, dtype,
+                                scale, causal, n_splits, stream)
 
 
 # ------------------------------------------------------------ tensor helpers
@@ -245,4 +273,90 @@ def fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False,
     _check(fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_scale.data_ptr(),
                       k_scale.data_ptr(), v_scale.data_ptr(), out.data_ptr(), lse.data_ptr(),
                       B, H, N, d, float(scale), int(bool(causal)), _stream(q8)))
+    return out, lse
+
+
+def _qkv_shapes(q, k, v):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    _check_tensor(q, "q", (B, H, Nq, d))
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(t, name, (B, H, Nk, d), q.dtype)
+    return B, H, Nq, Nk, d
+
+
+def fwd_partial(q, k, v, causal: bool = False, scale: float | None = None,
+                q_pos0: int = 0, k_pos0: int = 0, out=None, lse=None):
+    """Attention of q [B, H, Nq, d] over one key/value part k, v
+    [B, H, Nk, d]: (O_p fp32 normalised over the part, L_p fp32 log-sum-exp,
+    -inf where no key is visible).  Causal positions: query i at q_pos0 + i,
+    key j at k_pos0 + j."""
+    torch = _torch()
+    B, H, Nq, Nk, d = _qkv_shapes(q, k, v)
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+    _check_tensor(out, "out", (B, H, Nq, d), torch.float32)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_tensor(lse, "lse", (B, H, Nq), torch.float32)
+    _check(fa_fwd_partial(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                          out.data_ptr(), lse.data_ptr(), B, H, Nq, Nk, d, dt,
+                          float(scale), int(bool(causal)), int(q_pos0),
+                          int(k_pos0), _stream(q)))
+    return out, lse
+
+
+def merge(o_parts, lse_parts, dtype=None, out=None, lse=None):
+    """Log-sum-exp merge of partial results: o_parts [S, B, H, N, d] fp32,
+    lse_parts [S, B, H, N] fp32 -> (O [B, H, N, d] in `dtype` (bf16 by
+    default), LSE [B, H, N] fp32)."""
+    torch = _torch()
+    if o_parts.dim() != 5:
+        raise ValueError("o_parts must be [S, B, H, N, d]")
+    S, B, H, N, d = o_parts.shape
+    _check_tensor(o_parts, "o_parts", (S, B, H, N, d), torch.float32)
+    _check_tensor(lse_parts, "lse_parts", (S, B, H, N), torch.float32)
+    dtype = dtype or (out.dtype if out is not None else torch.bfloat16)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=dtype, device=o_parts.device)
+    _check_tensor(out, "out", (B, H, N, d), dtype)
+    dt = _dtype_code(out)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=o_parts.device)
+    _check_tensor(lse, "lse", (B, H, N), torch.float32)
+    _check(fa_merge(o_parts.data_ptr(), lse_parts.data_ptr(), S, out.data_ptr(),
+                    lse.data_ptr(), B, H, N, d, dt, _stream(o_parts)))
+    return out, lse
+
+
+def fwd_splitkv(q, k, v, n_splits: int, causal: bool = False,
+                scale: float | None = None, out=None, lse=None, workspace=None):
+    """Attention of q [B, H, Nq, d] over k, v [B, H, Nk, d] with the keys in
+    up to n_splits parts run in parallel and merged.  Causal aligns the
+    queries with the last Nq keys."""
+    torch = _torch()
+    B, H, Nq, Nk, d = _qkv_shapes(q, k, v)
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=q.dtype, device=q.device)
+    _check_tensor(out, "out", (B, H, Nq, d), q.dtype)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_tensor(lse, "lse", (B, H, Nq), torch.float32)
+    need = fa_splitkv_workspace_size(B, H, Nq, d, n_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    _check(fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                          out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+                          B, H, Nq, Nk, d, dt, float(scale), int(bool(causal)),
+                          int(n_splits), _stream(q)))
     return out, lse

@@ -142,6 +142,76 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            void* workspace, int B, int H, int N, int d, int dtype, float scale,
            int causal, void* stream);
 
+/*
+ * Split-KV attention: partial results over parts of the keys, and their
+ * log-sum-exp merge.  For a key set split into parts p, the attention of a
+ * query row over all keys is
+ *     L = ln sum_p exp(L_p),    O = sum_p exp(L_p - L) O_p,
+ * where O_p is the row's attention output over part p alone (normalised
+ * over that part) and L_p its log-sum-exp (-inf when no key of the part is
+ * visible; O_p is then 0).  This is the online softmax's rescaling applied
+ * across parts ("FlashAttention-3: Fast and Accurate Attention with
+ * Asynchrony and Low-precision", online-softmax description; Ring Attention
+ * and Lean Attention in its reference list combine per-device and
+ * per-split partials this way).
+ *
+ * Positions.  With causal = 1, query row i of q sits at global position
+ * q_pos0 + i, key row j of k at k_pos0 + j, and the key is visible iff its
+ * position <= the query's.  (q_pos0 = k_pos0 = 0 with equal lengths is
+ * fa_fwd's top-left mask.)
+ */
+
+/*
+ * fa_fwd_partial -- attention of q over one key/value part.
+ *   q        : [B][H][Nq][d] of `dtype`;  k, v : [B][H][Nk][d] of `dtype`.
+ *   o        : [B][H][Nq][d] float, written: O_p (fp32, normalised over
+ *              the part; 0 for rows that see no key of the part).
+ *   lse      : [B][H][Nq] float, written: L_p (natural log; -inf for rows
+ *              that see no key).  Required (it is the merge's input).
+ *   Nq, Nk   : >= 1, <= 2^29.  q_pos0, k_pos0 : >= 0, <= 2^29.
+ *   Other arguments as in fa_fwd.
+ */
+int fa_fwd_partial(const void* q, const void* k, const void* v, float* o,
+                   float* lse, int B, int H, int Nq, int Nk, int d, int dtype,
+                   float scale, int causal, int q_pos0, int k_pos0,
+                   void* stream);
+
+/*
+ * fa_merge -- combine n_parts partial results into the attention output.
+ *   o_parts   : [n_parts][B][H][N][d] float (part p's O_p), read only.
+ *   lse_parts : [n_parts][B][H][N] float (part p's L_p), read only.
+ *   o         : [B][H][N][d] of `dtype`, written (rounded to nearest even).
+ *   lse       : [B][H][N] float, written (L), or NULL.
+ *   n_parts   : >= 1.  Parts whose L_p is -inf contribute nothing (their
+ *               O_p is not used).  A row with every L_p = -inf gets O = 0
+ *               and L = -inf.
+ */
+int fa_merge(const float* o_parts, const float* lse_parts, int n_parts,
+             void* o, float* lse, int B, int H, int N, int d, int dtype,
+             void* stream);
+
+/*
+ * fa_fwd_splitkv -- attention of Nq queries over Nk keys, the keys split
+ * into up to n_splits parts that run as independent workgroups (more
+ * parallelism when Nq is small, as in decoding), then merged.
+ *   q : [B][H][Nq][d];  k, v : [B][H][Nk][d];  o : [B][H][Nq][d] (`dtype`).
+ *   lse       : [B][H][Nq] float or NULL.
+ *   workspace : device memory of at least
+ *               fa_splitkv_workspace_size(B, H, Nq, d, n_splits) bytes,
+ *               16-byte aligned; contents on entry ignored, on exit
+ *               unspecified.
+ *   n_splits  : >= 1.  Parts are ceil(Nk / n_splits) keys rounded up to a
+ *               multiple of 64, so fewer parts may be used.
+ *   causal    : 1 aligns the queries with the last Nq keys (query i at
+ *               position Nk - Nq + i, key j at j): the decoding convention,
+ *               and fa_fwd's mask when Nq = Nk.
+ */
+size_t fa_splitkv_workspace_size(int B, int H, int Nq, int d, int n_splits);
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
+                   float* lse, void* workspace, int B, int H, int Nq, int Nk,
+                   int d, int dtype, float scale, int causal, int n_splits,
+                   void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_str(int status);
 

@@ -28,6 +28,18 @@ accumulator named in the FlashAttention-3 Appendix B fragment (exp2, row_sum
 and O rescaling).  It is written out here only so that tests can check that
 the recurrence reaches the materialising result; the GPU does not use it.
 
+Split-KV (``attention_fwd_positions``, ``merge_partials``): attention of
+N_q queries over N_k keys at explicit positions -- query i at q_pos0 + i, key
+j at k_pos0 + j, the key visible under the causal mask iff its position is
+not after the query's -- is the same definition with that mask; a row that
+sees no key has no softmax, and is given O = 0 and LSE = -inf (the identity
+element of the merge below).  Partial results over parts of the keys combine
+as L = ln sum_p exp(L_p), O = sum_p exp(L_p - L) O_p: the online softmax's
+rescaling (FlashAttention-4 related-papers page, online-softmax snippet)
+applied across parts, which Ring Attention and Lean Attention (reference list
+of the FlashAttention-3 page) use to combine per-device and per-split
+results.  The merge is checked against the definition over all keys.
+
 All arrays are [B, H, N, d]; inputs of any float dtype are widened to fp64.
 """
 
@@ -39,6 +51,9 @@ import numpy as np
 
 __all__ = [
     "attention_fwd",
+    "attention_fwd_positions",
+    "attention_fwd_positions_rows",
+    "merge_partials",
     "attention_bwd",
     "attention_fwd_loops",
     "attention_fwd_online",
@@ -231,4 +246,80 @@ def attention_fwd_online(q, k, v, causal: bool = False,
                 m = m_new
             o[b, h] = acc / l[:, None]
             lse[b, h] = (m * math.log(2.0) if base2 else m) + np.log(l)
+    return o, lse
+
+
+def _positions_block(qb, k, v, scale, qpos, kpos, causal):
+    """(O, LSE) of query rows at positions qpos against all keys k, v."""
+    s = (qb @ k.T) * scale
+    if causal:
+        s = np.where(kpos[None, :] > qpos[:, None], -np.inf, s)
+    m = s.max(axis=1)
+    empty = ~np.isfinite(m)          # every key masked (or no key at all)
+    m_safe = np.where(empty, 0.0, m)
+    e = np.exp(s - m_safe[:, None])  # exp(-inf) = 0 for masked keys
+    l = e.sum(axis=1)
+    l_safe = np.where(empty, 1.0, l)
+    o = (e / l_safe[:, None]) @ v
+    o[empty] = 0.0
+    lse = np.where(empty, -np.inf, m_safe + np.log(l_safe))
+    return o, lse
+
+
+def attention_fwd_positions(q, k, v, causal: bool = False,
+                            scale: float | None = None, q_pos0: int = 0,
+                            k_pos0: int = 0, row_block: int = 1024):
+    """Attention of q [B,H,Nq,d] over k, v [B,H,Nk,d] with query i at
+    position q_pos0 + i and key j at k_pos0 + j (causal: visible iff
+    k_pos0 + j <= q_pos0 + i).  Rows that see no key: O = 0, LSE = -inf.
+    Returns (O [B,H,Nq,d], LSE [B,H,Nq]) in fp64."""
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = default_scale(d)
+    kpos = k_pos0 + np.arange(Nk)
+    o = np.empty_like(q)
+    lse = np.empty((B, H, Nq), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, Nq, row_block):
+                r1 = min(Nq, r0 + row_block)
+                qpos = q_pos0 + np.arange(r0, r1)
+                o[b, h, r0:r1], lse[b, h, r0:r1] = _positions_block(
+                    q[b, h, r0:r1], k[b, h], v[b, h], scale, qpos, kpos, causal)
+    return o, lse
+
+
+def attention_fwd_positions_rows(q, k, v, rows, causal: bool = False,
+                                 scale: float | None = None, q_pos0: int = 0,
+                                 k_pos0: int = 0):
+    """``attention_fwd_positions`` for selected query rows of one head
+    (q [Nq, d], k, v [Nk, d]).  Returns (O [len(rows), d], LSE [len(rows)])."""
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    if scale is None:
+        scale = default_scale(q.shape[1])
+    rows = np.asarray(rows, dtype=np.int64)
+    kpos = k_pos0 + np.arange(k.shape[0])
+    return _positions_block(q[rows], k, v, scale, q_pos0 + rows, kpos, causal)
+
+
+def merge_partials(o_parts, lse_parts):
+    """Combine partial attention results over parts of the keys.
+
+    o_parts [S, ..., d] (each part's O, normalised over its keys), lse_parts
+    [S, ...] (each part's LSE, -inf for a part that row cannot see):
+        L = ln sum_p exp(L_p),   O = sum_p exp(L_p - L) O_p.
+    Parts with L_p = -inf get weight 0 and their O_p is not read; a row with
+    every L_p = -inf gets O = 0, L = -inf.  Returns (O, L) in fp64."""
+    o_parts, lse_parts = _as64(o_parts), _as64(lse_parts)
+    m = lse_parts.max(axis=0)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    w = np.exp(lse_parts - m_safe[None])            # 0 for empty parts
+    wsum = w.sum(axis=0)
+    contrib = np.where((w > 0)[..., None], o_parts, 0.0) * w[..., None]
+    o = contrib.sum(axis=0) / np.where(empty, 1.0, wsum)[..., None]
+    o[empty] = 0.0
+    lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, wsum)))
     return o, lse

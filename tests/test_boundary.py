@@ -42,7 +42,8 @@ def fa():
 def test_header_declares_expected_entry_points():
     d = _declared()
     assert {"fa_fwd", "fa_quant_fp8", "fa_fwd_fp8", "fa_bwd",
-            "fa_bwd_workspace_size", "fa_status_str"} <= set(d)
+            "fa_bwd_workspace_size", "fa_status_str", "fa_fwd_partial", "fa_merge",
+            "fa_splitkv_workspace_size", "fa_fwd_splitkv"} <= set(d)
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -115,6 +116,38 @@ def test_bwd_rejects_and_workspace(fa):
         a = dict(base)
         a.update(kw)
         assert fa.fa_bwd(**a) == code, kw
+
+
+def test_splitkv_entry_points_reject(fa):
+    base = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, Nq=4, Nk=100, d=128,
+                dtype=0, scale=0.1, causal=1, q_pos0=96, k_pos0=0, stream=None)
+    for kw, code in ((dict(q=None), -1), (dict(lse=None), -1), (dict(o=FAKE + 4), -1),
+                     (dict(Nq=0), -1), (dict(Nk=-1), -1), (dict(Nk=(1 << 29) + 1), -1),
+                     (dict(q_pos0=-1), -1), (dict(k_pos0=(1 << 29) + 1), -1),
+                     (dict(causal=3), -1), (dict(scale=0.0), -1), (dict(dtype=4), -1),
+                     (dict(d=80), -2)):
+        a = dict(base)
+        a.update(kw)
+        assert fa.fa_fwd_partial(**a) == code, kw
+    base = dict(o_parts=FAKE, lse_parts=FAKE, n_parts=3, o=FAKE, lse=None, B=1, H=2, N=16,
+                d=64, dtype=0, stream=None)
+    for kw, code in ((dict(o_parts=None), -1), (dict(lse_parts=None), -1), (dict(o=None), -1),
+                     (dict(n_parts=0), -1), (dict(N=0), -1), (dict(o_parts=FAKE + 4), -1),
+                     (dict(lse=FAKE + 1), -1), (dict(dtype=9), -1), (dict(d=100), -2)):
+        a = dict(base)
+        a.update(kw)
+        assert fa.fa_merge(**a) == code, kw
+    assert fa.fa_splitkv_workspace_size(2, 4, 1, 128, 8) == 2 * 4 * 1 * 8 * 129 * 4
+    assert fa.fa_splitkv_workspace_size(2, 4, 1, 128, 0) == 0
+    assert fa.fa_splitkv_workspace_size(2, 4, 1, 96, 8) == 0
+    base = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, ws=FAKE, B=1, H=1, Nq=1, Nk=100,
+                d=64, dtype=1, scale=0.1, causal=0, n_splits=4, stream=None)
+    for kw, code in ((dict(ws=None), -1), (dict(ws=FAKE + 8), -1), (dict(n_splits=0), -1),
+                     (dict(Nq=-2), -1), (dict(k=None), -1), (dict(causal=5), -1),
+                     (dict(d=512), -2)):
+        a = dict(base)
+        a.update(kw)
+        assert fa.fa_fwd_splitkv(**a) == code, kw
 
 
 def test_python_helpers_reject_bad_tensors(fa):
