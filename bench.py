@@ -10,6 +10,21 @@ d=128; i.i.d. N(0,1) inputs, resident in HBM before timing starts):
   fwd_fp8    fa_fwd_fp8, non-causal                    4*B*H*N^2*d flop
   bwd_bf16   fa_bwd, non-causal                    2.5*4*B*H*N^2*d flop
 
+The rows beyond the hot path are timed separately, after the steps, and
+reported under "next_rows" (they do not enter ``value``):
+
+  fwd_causal_persistent  fa_fwd causal at the same shape with the persistent
+                         heaviest-first grid, beside per-tile dispatch
+                         (FA_FWD_SCHED=1)                 2*B*H*N^2*d flop
+  ring_pass_4_chunks     four fa_fwd_partial calls (causal key chunks of N/4
+                         at their positions) + fa_merge   2*B*H*N^2*d flop
+  blocksparse_window     fa_fwd_blocksparse causal, each 128-row block sees
+                         its own and two previous 128-key blocks and block 0
+                                                 4*d*(visible pairs) flop
+  splitkv_decode         fa_fwd_splitkv, B=16, H=16, one query over 16,384
+                         keys, d=128, 16 parts: HBM-bound, algorithmic bytes
+                         = K and V read once (+ Q, O, LSE)
+
 Legs whose entry point is not built yet report FA_ERR_UNSUPPORTED at start-up
 and are left out of the step (listed under "legs_missing").  ``value`` is the
 step's attention flop divided by its wall time (HIP events on the launch
@@ -19,6 +34,7 @@ in the same JSON line, next to the fp64 oracle timed on a bounded sample on
 the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                      [--no-next-rows]
 """
 
 from __future__ import annotations
@@ -141,7 +157,170 @@ def build_legs(torch, fa, dev):
     # (and its roofline reported) as that one launch sequence.
     legs.append(dict(name="bwd_bf16", call=bwd_call, flops=2.5 * fwd_flops(B, H, N, d),
                      dtype="bf16", kernel="bwd_pre_kernel+bwd_kv2_kernel+bwd_dq_kernel"))
-    return legs
+    return legs, (qd, kd, vd)
+
+
+def build_next_rows(torch, fa, dev, fwd_inputs):
+    """Rows beyond the hot path: (name, call, flops, bytes, kernel, config,
+    before, after); before/after run around each timed launch sequence on the
+    host (environment switches), outside the events."""
+    qd, kd, vd = fwd_inputs
+    B, H, N, d = (WORKLOAD[k] for k in "BHNd")
+    scale = 1.0 / math.sqrt(d)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    rows = []
+
+    def causal_call():
+        return fa.fa_fwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(),
+                         lse.data_ptr(), B, H, N, d, fa.FA_BF16, scale, 1, stream)
+
+    def sched(value):
+        def set_env():
+            if value is None:
+                os.environ.pop("FA_FWD_SCHED", None)
+            else:
+                os.environ["FA_FWD_SCHED"] = value
+        return set_env
+    rows.append(dict(name="fwd_causal_persistent", call=causal_call,
+                     flops=fwd_flops(B, H, N, d, True), bytes=None, kernel="fwd_kernel",
+                     config=f"B={B} H={H} N={N} d={d} causal", before=sched(None),
+                     after=sched(None)))
+    rows.append(dict(name="fwd_causal_per_tile", call=causal_call,
+                     flops=fwd_flops(B, H, N, d, True), bytes=None, kernel="fwd_kernel",
+                     config=f"B={B} H={H} N={N} d={d} causal, FA_FWD_SCHED=1",
+                     before=sched("1"), after=sched(None)))
+
+    G = 4
+    c = N // G
+    kc = [kd[:, :, g * c:(g + 1) * c].contiguous() for g in range(G)]
+    vc = [vd[:, :, g * c:(g + 1) * c].contiguous() for g in range(G)]
+    o_parts = torch.empty((G, B, H, N, d), dtype=torch.float32, device=dev)
+    lse_parts = torch.empty((G, B, H, N), dtype=torch.float32, device=dev)
+
+    def ring_call():
+        for g in range(G):
+            rc = fa.fa_fwd_partial(qd.data_ptr(), kc[g].data_ptr(), vc[g].data_ptr(),
+                                   o_parts[g].data_ptr(), lse_parts[g].data_ptr(), B, H, N, c,
+                                   d, fa.FA_BF16, scale, 1, 0, g * c, stream)
+            if rc != fa.FA_OK:
+                return rc
+        return fa.fa_merge(o_parts.data_ptr(), lse_parts.data_ptr(), G, o.data_ptr(),
+                           lse.data_ptr(), B, H, N, d, fa.FA_BF16, stream)
+    rows.append(dict(name="ring_pass_4_chunks", call=ring_call,
+                     flops=fwd_flops(B, H, N, d, True), bytes=None,
+                     kernel="fwd_kernel (partial) x4 + merge_kernel",
+                     config=f"B={B} H={H} N={N} d={d} causal, keys in 4 chunks",
+                     before=None, after=None))
+
+    # Block-sparse: each 128-row query block attends to its own and the two
+    # previous key blocks and to key block 0 (sliding window + global
+    # column), causal.  Flops count the visible (query, key) pairs only.
+    import numpy as np
+    nb = -(-N // 128)
+    m = np.zeros((nb, nb), np.uint8)
+    for i in range(nb):
+        m[i, max(0, i - 2):i + 1] = 1
+        m[i, 0] = 1
+    rows_i = np.arange(N)
+    visible = 0
+    for i in range(nb):
+        r = rows_i[i * 128:(i + 1) * 128]
+        for j in np.nonzero(m[i])[0]:
+            c0, c1 = j * 128, min(N, (j + 1) * 128)
+            visible += int(np.clip(r[:, None] - np.arange(c0, c1)[None, :] + 1, 0, 1).sum())
+    bmask = torch.from_numpy(np.broadcast_to(m, (H, nb, nb)).copy()).to(dev)
+    bws = torch.empty((max(fa.fa_blocksparse_workspace_size(B, H, N, d, 0), 16),),
+                      dtype=torch.uint8, device=dev)
+
+    def sparse_call():
+        return fa.fa_fwd_blocksparse(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(),
+                                     lse.data_ptr(), bmask.data_ptr(), 0, bws.data_ptr(), B, H,
+                                     N, d, fa.FA_BF16, scale, 1, stream)
+    rows.append(dict(name="blocksparse_window", call=sparse_call,
+                     flops=4.0 * d * visible * B * H, bytes=None,
+                     kernel="bs_index_kernel + fwd_kernel (sparse)",
+                     config=f"B={B} H={H} N={N} d={d} causal, 128-blocks: window of 3 + "
+                            f"global column ({m.sum()} of {nb * nb} blocks)",
+                     before=None, after=None))
+
+    # Decoding: seeded device-side N(0,1) draws (torch's generator; the values
+    # do not change the work).
+    DB, DH, DNq, DNk, S = 16, 16, 1, 16384, 16
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 * WORKLOAD_ID + 7)
+    qd1 = torch.randn((DB, DH, DNq, d), generator=gen, device=dev).to(torch.bfloat16)
+    kd1 = torch.randn((DB, DH, DNk, d), generator=gen, device=dev).to(torch.bfloat16)
+    vd1 = torch.randn((DB, DH, DNk, d), generator=gen, device=dev).to(torch.bfloat16)
+    od1 = torch.empty_like(qd1)
+    ld1 = torch.empty((DB, DH, DNq), dtype=torch.float32, device=dev)
+    wsz = fa.fa_splitkv_workspace_size(DB, DH, DNq, d, S)
+    ws1 = torch.empty((max(wsz, 16),), dtype=torch.uint8, device=dev)
+
+    def decode_call():
+        return fa.fa_fwd_splitkv(qd1.data_ptr(), kd1.data_ptr(), vd1.data_ptr(),
+                                 od1.data_ptr(), ld1.data_ptr(), ws1.data_ptr(), DB, DH, DNq,
+                                 DNk, d, fa.FA_BF16, scale, 1, S, stream)
+    kv_bytes = 2 * DB * DH * DNk * d * 2
+    rows.append(dict(name="splitkv_decode", call=decode_call,
+                     flops=fwd_flops(DB, DH, 1, d) * DNk,  # 4*Nk*d per query row
+                     bytes=kv_bytes + 2 * DB * DH * DNq * d * 2 + DB * DH * DNq * 4,
+                     kernel="fwd_kernel (partial) + merge_kernel",
+                     config=f"B={DB} H={DH} Nq={DNq} Nk={DNk} d={d} causal, {S} parts",
+                     before=None, after=None))
+    return rows
+
+
+def time_next_rows(torch, fa, rows, steps, warmup, rounds=5):
+    """Median per-call time of each row over `rounds` rounds that visit the
+    rows in turn (so that clock and thermal drift hit every row alike)."""
+    live = []
+    report = {}
+    for r in rows:
+        if r["before"]:
+            r["before"]()
+        rc = r["call"]()
+        if r["after"]:
+            r["after"]()
+        if rc == fa.FA_ERR_UNSUPPORTED:
+            report[r["name"]] = None
+            continue
+        if rc != fa.FA_OK:
+            raise fa.FaError(rc)
+        live.append(r)
+    times = {r["name"]: [] for r in live}
+    for _ in range(rounds):
+        for r in live:
+            if r["before"]:
+                r["before"]()
+            for _ in range(warmup):
+                r["call"]()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(steps):
+                r["call"]()
+            b.record()
+            torch.cuda.synchronize()
+            if r["after"]:
+                r["after"]()
+            times[r["name"]].append(a.elapsed_time(b) / steps)
+    for r in live:
+        ts = sorted(times[r["name"]])
+        ms = ts[len(ts) // 2]
+        rec = {"ms": round(ms, 4), "config": r["config"], "kernel": r["kernel"]}
+        if r["bytes"]:
+            gbps = r["bytes"] / (ms * 1e-3) / 1e9
+            rec.update({"bound": "hbm", "gbps": round(gbps, 1),
+                        "frac_of_hbm": round(gbps / HBM_GBPS, 4),
+                        "algorithmic_bytes": r["bytes"]})
+        else:
+            tf = r["flops"] / (ms * 1e-3) / 1e12
+            rec.update({"bound": "mfma", "tflops": round(tf, 2),
+                        "frac_of_peak": round(tf / PEAK_TFLOPS["bf16"], 4)})
+        report[r["name"]] = rec
+    return report
 
 
 def cpu_baseline(legs_present, budget_s=15.0):
@@ -193,6 +372,8 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the rows beyond the hot path")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one device copy of this many MiB "
@@ -212,7 +393,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     fa.lib()
-    legs_all = build_legs(torch, fa, dev)
+    legs_all, fwd_inputs = build_legs(torch, fa, dev)
     torch.cuda.synchronize()
 
     # Keep the legs whose entry point is built; any other failure is fatal.
@@ -267,6 +448,11 @@ def main():
     leg_ms = {n: sum(a.elapsed_time(b) for a, b in zip(*ev)) / len(ev[0])
               for n, ev in events.items()}
 
+    next_rows = None
+    if not args.no_next_rows:
+        next_rows = time_next_rows(torch, fa, build_next_rows(torch, fa, dev, fwd_inputs),
+                                   10, 3)
+
     if args.calib_copy_mib:
         src = torch.empty(args.calib_copy_mib * 2**20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -318,6 +504,8 @@ def main():
         "legs": leg_report,
         "roofline": roofline,
     }
+    if next_rows is not None:
+        out["next_rows"] = next_rows
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline({l["name"] for l in legs}, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -160,6 +160,38 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   return launch_status(fa::launch_merge(m, d, dtype, s));
 }
 
+size_t fa_blocksparse_workspace_size(int B, int H, int N, int d, int mask_per_batch) {
+  if (!valid_dims(B, H, N) || !supported_d(d) || (mask_per_batch != 0 && mask_per_batch != 1))
+    return 0;
+  return fa::sparse_list_bytes(mask_per_batch ? B * H : H, N, d);
+}
+
+int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                       const void* block_mask, int mask_per_batch, void* workspace, int B, int H,
+                       int N, int d, int dtype, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !block_mask || !workspace) return FA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse) ||
+      !aligned4(workspace))
+    return FA_ERR_INVALID;
+  if (!valid_dims(B, H, N) || (dtype != FA_BF16 && dtype != FA_FP16)) return FA_ERR_INVALID;
+  if (mask_per_batch != 0 && mask_per_batch != 1) return FA_ERR_INVALID;
+  if (!valid_scale(scale) || (causal != 0 && causal != 1)) return FA_ERR_INVALID;
+  if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+  fa::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.N = N;
+  a.bs_per_batch = mask_per_batch;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return launch_status(fa::launch_fwd_sparse(a, B, H, d, dtype, causal != 0,
+                                             static_cast<const uint8_t*>(block_mask),
+                                             static_cast<int*>(workspace),
+                                             static_cast<hipStream_t>(stream)));
+}
+
 int fa_quant_fp8(const void* x, int dtype, void* x8, float* scales, const float* signs,
                  float scale_mul, int per_tensor, int B, int H, int N, int d, void* stream) {
   if (!x || !x8 || !scales) return FA_ERR_INVALID;

@@ -104,10 +104,14 @@ __device__ __forceinline__ void persistent_units(const FwdArgs& a, F&& run) {
 // [s k_chunk, (s+1) k_chunk) only and writes O normalised over those keys in
 // fp32 and their log-sum-exp to slot s of the partial outputs; a merge kernel
 // combines the slots.
+// SPARSE: block-sparse mode.  bs_list holds, per (mask head, query tile), the
+// number of live key tiles and their list (see bs_index_kernel); the tile
+// loop walks that list instead of every key tile, and a wave masks a listed
+// tile out entirely when its own 128-row query block does not attend to it.
 template <int D, int BN, int NW, int QB, int OCC, int NSTG, bool CAUSAL, int DT, bool PERSIST,
-          bool PARTIAL>
+          bool PARTIAL, bool SPARSE>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
-fwd_kernel(FwdArgs a) {
+fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
   using E = Elem<DT>;
   using v8 = typename E::v8;
   constexpr int WQ = 32 * QB;        // query rows per wave
@@ -153,7 +157,21 @@ fwd_kernel(FwdArgs a) {
   const int q0 = qt * BM;
   const int qw0 = q0 + wave * WQ;  // first query row of this wave
   const int kend = CAUSAL ? max(min(kn, q0 + BM + coff), 0) : kn;
-  const int ntiles = (kend + BN - 1) / BN;
+  // Block-sparse: entry e of the list is key tile (e & 0xffffff), with bit
+  // 24 + b set when query block b of the tile (rows q0 + 128 b ...) attends
+  // to it.  The list is followed by padding entries that name a tile past the
+  // last key (zeros, fully masked) with no bits, so that the reads below,
+  // which run up to a few positions past the end, need no bounds check (a
+  // branch there would break the straight-line schedule of the loop).
+  const int* lst = nullptr;
+  int nlist = 0;
+  if constexpr (SPARSE) {
+    const int mh = a.bs_per_batch ? bh : bh % a.heads;
+    lst = bs_list + ((int64_t)mh * a.n_qtiles + qt) * a.bs_stride;
+    nlist = lst[0];
+  }
+  auto tile_of = [&](int j) { return lst[1 + j] & 0xffffff; };
+  const int ntiles = SPARSE ? nlist : (kend + BN - 1) / BN;
   const float c = a.scale_log2;
 
   // ---- Copies.  Copy jj of this wave fills LDS chunk (wave*IPW + jj)*64 + lane
@@ -168,6 +186,10 @@ fwd_kernel(FwdArgs a) {
     dma_voff[jj] = (uint32_t)((p / CH_ROW) * ROWB + ((p % CH_ROW) ^ swz<D>(p / CH_ROW)) * 16);
   }
   auto issue = [&](const uint16_t* src, int t, FA_LDS uint8_t* stage) {
+    if constexpr (SPARSE) {
+      const int tt = tile_of(max(t, 0));
+      t = t < 0 ? t : tt;
+    }
     const int rows = t < 0 ? 0 : min(max(kn - t * BN, 0), BN);
     const u32x4_t r = make_rsrc(src + (int64_t)t * BN * D, rows * ROWB);
 #pragma unroll
@@ -344,6 +366,7 @@ fwd_kernel(FwdArgs a) {
   int t_mask = (kn % BN) ? kn / BN : ntiles;
   if (CAUSAL) t_mask = min(t_mask, max(q0 + coff + 1, 0) / BN);
   t_mask = min(t_mask, ntiles);
+  if constexpr (SPARSE) t_mask = 0;  // every listed tile may be masked for some wave
 
   Scores sA, sB;
   Probs pA, pB;
@@ -425,11 +448,15 @@ fwd_kernel(FwdArgs a) {
     if constexpr (DS && MS) {
       // Register r of block kb holds key t*BN + 4*hl + (kb*32 + 8*(r/4) + r%4)
       // with t = j+1; it is visible iff that constant offset is below `lim`.
-      const int t = j + 1;
+      const int t = SPARSE ? tile_of(j + 1) : j + 1;
+      // Block-sparse: the wave's query block does not attend to this tile.
+      bool dead = false;
+      if constexpr (SPARSE) dead = !((lst[2 + j] >> (24 + (wave * WQ) / 128)) & 1);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         int lim = kn - t * BN - 4 * hl;
         if (CAUSAL) lim = min(lim, qw0 + 32 * qb + l32 + 1 + coff - t * BN - 4 * hl);
+        if (dead) lim = -BN;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -562,6 +589,20 @@ template <> struct FwdCfg<128> { static constexpr int BN = 64, NW = 8, QB = 1, O
 #endif
 template <> struct FwdCfg<256> { static constexpr int BN = 32, NW = 4, QB = 1, OCC = 1, NSTG = 3; };
 
+// Block-sparse list geometry per head dimension: query tiles per head and
+// ints per list (count, one entry per key tile, kSparsePad padding entries:
+// the pipeline reads up to four positions past the last live tile).
+constexpr int kSparsePad = 6;
+template <int D>
+int sparse_qtiles(int N) {
+  constexpr int BM = 32 * FwdCfg<D>::QB * FwdCfg<D>::NW;
+  return (N + BM - 1) / BM;
+}
+template <int D>
+int sparse_list_stride(int N) {
+  return (N + FwdCfg<D>::BN - 1) / FwdCfg<D>::BN + 1 + kSparsePad;
+}
+
 // Workgroups of `kernel` resident at once on the current device.
 template <typename K>
 int query_resident_slots(K kernel, int threads) {
@@ -572,8 +613,9 @@ int query_resident_slots(K kernel, int threads) {
   return cus * per_cu;
 }
 
-template <int D, bool CAUSAL, bool PERSIST, bool PARTIAL, int DT>
-hipError_t launch_one(const FwdArgs& a, int BH, hipStream_t stream) {
+template <int D, bool CAUSAL, bool PERSIST, bool PARTIAL, int DT, bool SPARSE = false>
+hipError_t launch_one(const FwdArgs& a, int BH, hipStream_t stream,
+                      const int* bs_list = nullptr) {
   using C = FwdCfg<D>;
   constexpr int BM = 32 * C::QB * C::NW;
   FwdArgs args = a;
@@ -581,7 +623,8 @@ hipError_t launch_one(const FwdArgs& a, int BH, hipStream_t stream) {
   args.bh = BH;
   const int64_t units = (int64_t)args.n_qtiles * BH * args.n_split;
   if (units > 0x7fffffff) return hipErrorInvalidValue;
-  auto kernel = fwd_kernel<D, C::BN, C::NW, C::QB, C::OCC, C::NSTG, CAUSAL, DT, PERSIST, PARTIAL>;
+  auto kernel =
+      fwd_kernel<D, C::BN, C::NW, C::QB, C::OCC, C::NSTG, CAUSAL, DT, PERSIST, PARTIAL, SPARSE>;
   int64_t grid = units;
   if constexpr (PERSIST) {
     // Device property cache, filled once per device and instantiation.
@@ -598,7 +641,7 @@ hipError_t launch_one(const FwdArgs& a, int BH, hipStream_t stream) {
     grid = std::min<int64_t>(units, slots);
     args.pin = (BH % 8 == 0 && grid % 8 == 0) ? 1 : 0;
   }
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(C::NW * 64), 0, stream, args);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(C::NW * 64), 0, stream, args, bs_list);
   return hipGetLastError();
 }
 
@@ -639,7 +682,102 @@ hipError_t launch_partial_dtype(const FwdArgs& a, int BH, int d, bool causal, hi
   }
 }
 
+// Live key tiles of each (mask head, query tile) of the block-sparse forward:
+// out[0] = count, out[1 + i] = key tile | (query-block bits << 24), in
+// increasing tile order, then kSparsePad entries naming the first tile past
+// the last key with no bits.  A key tile is live when some 128-row query block of
+// the workgroup's tile attends to its 128-key block (and, when causal, the
+// tile is not wholly above the diagonal).  One thread per list.
+template <int D>
+__global__ void __launch_bounds__(256)
+bs_index_kernel(const uint8_t* __restrict__ mask, int* __restrict__ out, int n_lists,
+                int n_qtiles, int N, int stride, int causal) {
+  using C = FwdCfg<D>;
+  constexpr int BM = 32 * C::QB * C::NW;
+  constexpr int BN = C::BN;
+  constexpr int QBW = BM / kSparseBlock;  // query blocks per workgroup tile
+  static_assert(BM % kSparseBlock == 0 && kSparseBlock % BN == 0, "sparse block sizes");
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= n_lists) return;
+  const int mh = (int)(gid / n_qtiles);
+  const int qt = (int)(gid % n_qtiles);
+  const int nb = (N + kSparseBlock - 1) / kSparseBlock;
+  const int nkt = (N + BN - 1) / BN;
+  const int q0 = qt * BM;
+  const int qlast = min(q0 + BM, N) - 1;
+  const uint8_t* mrow = mask + (int64_t)mh * nb * nb;
+  int* o = out + gid * stride;
+  int count = 0;
+  for (int t = 0; t < nkt; ++t) {
+    if (causal && t * BN > qlast) break;
+    const int kb = t * BN / kSparseBlock;
+    int bits = 0;
+#pragma unroll
+    for (int b = 0; b < QBW; ++b) {
+      const int qblk = q0 / kSparseBlock + b;
+      if (qblk < nb && mrow[(int64_t)qblk * nb + kb] != 0) bits |= 1 << b;
+    }
+    if (bits) o[1 + count++] = t | (bits << 24);
+  }
+  for (int i = 0; i < kSparsePad; ++i) o[1 + count + i] = nkt;
+  o[0] = count;
+}
+
+template <int D, int DT>
+hipError_t launch_sparse_d(const FwdArgs& a, int BH, bool causal, const uint8_t* mask,
+                           int* list, hipStream_t s) {
+  using C = FwdCfg<D>;
+  constexpr int BM = 32 * C::QB * C::NW;
+  FwdArgs args = a;
+  const int n_qtiles = (a.N + BM - 1) / BM;
+  args.bs_stride = sparse_list_stride<D>(a.N);
+  const int64_t n_lists = (int64_t)(a.bs_per_batch ? BH : a.heads) * n_qtiles;
+  const int64_t blocks = (n_lists + 255) / 256;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bs_index_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, s, mask, list,
+                     (int)n_lists, n_qtiles, a.N, args.bs_stride, causal ? 1 : 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return causal ? launch_one<D, true, false, false, DT, true>(args, BH, s, list)
+                : launch_one<D, false, false, false, DT, true>(args, BH, s, list);
+}
+
+template <int DT>
+hipError_t launch_sparse_dtype(const FwdArgs& a, int BH, int d, bool causal, const uint8_t* mask,
+                               int* list, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_sparse_d<64, DT>(a, BH, causal, mask, list, s);
+    case 128: return launch_sparse_d<128, DT>(a, BH, causal, mask, list, s);
+    case 256: return launch_sparse_d<256, DT>(a, BH, causal, mask, list, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
+
+size_t sparse_list_bytes(int n_mask_heads, int N, int d) {
+  int stride = 0, n_qtiles = 0;
+  switch (d) {
+    case 64: stride = sparse_list_stride<64>(N); n_qtiles = sparse_qtiles<64>(N); break;
+    case 128: stride = sparse_list_stride<128>(N); n_qtiles = sparse_qtiles<128>(N); break;
+    case 256: stride = sparse_list_stride<256>(N); n_qtiles = sparse_qtiles<256>(N); break;
+    default: return 0;
+  }
+  return (size_t)n_mask_heads * n_qtiles * stride * sizeof(int);
+}
+
+hipError_t launch_fwd_sparse(const FwdArgs& a0, int B, int H, int d, int dtype, bool causal,
+                             const uint8_t* mask, int* list, hipStream_t stream) {
+  FwdArgs a = a0;
+  a.Nk = a.N;
+  a.c_off = 0;
+  a.k_chunk = a.N;
+  a.n_split = 1;
+  a.heads = H;
+  const int BH = B * H;
+  return dtype == 0 ? launch_sparse_dtype<0>(a, BH, d, causal, mask, list, stream)
+                    : launch_sparse_dtype<1>(a, BH, d, causal, mask, list, stream);
+}
 
 hipError_t launch_fwd(const FwdArgs& a0, int B, int H, int d, int dtype, bool causal,
                       hipStream_t stream) {

@@ -25,7 +25,14 @@ struct FwdArgs {
   int n_split;       // splits: split s covers keys [s k_chunk, (s+1) k_chunk)
   float* o32;        // [n_split][B][H][N][d] fp32, O normalised within the split
   float* lse32;      // [n_split][B][H][N], log-sum-exp within the split (-inf if empty)
+  // Block-sparse (launch_fwd_sparse):
+  int heads;         // H
+  int bs_per_batch;  // mask is [B][H][nb][nb] (1) or [H][nb][nb] (0)
+  int bs_stride;     // ints per live-tile list (launcher)
 };
+
+// Rows and keys per block of the block-sparse mask.
+constexpr int kSparseBlock = 128;
 
 // Enqueue the 16-bit forward.  Arguments are validated by the caller.
 hipError_t launch_fwd(const FwdArgs& a, int B, int H, int d, int dtype, bool causal,
@@ -34,6 +41,12 @@ hipError_t launch_fwd(const FwdArgs& a, int B, int H, int d, int dtype, bool cau
 // Enqueue the split-KV partial forward (fp32 partial outputs per split).
 hipError_t launch_fwd_partial(const FwdArgs& a, int B, int H, int d, int dtype, bool causal,
                               hipStream_t stream);
+
+// Enqueue the block-sparse forward: builds the live-tile lists in `list`
+// (sparse_list_bytes bytes) from the block mask, then the forward over them.
+hipError_t launch_fwd_sparse(const FwdArgs& a, int B, int H, int d, int dtype, bool causal,
+                             const uint8_t* mask, int* list, hipStream_t stream);
+size_t sparse_list_bytes(int n_mask_heads, int N, int d);
 
 struct MergeArgs {
   const float* o_parts;    // [S][rows][d] fp32

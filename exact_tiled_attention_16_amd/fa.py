@@ -45,6 +45,9 @@ SIGNATURES = {
     "fa_splitkv_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "fa_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F,
                             _I, _I, _P]),
+    "fa_blocksparse_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "fa_fwd_blocksparse": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I,
+                                _F, _I, _P]),
     "fa_status_str": (ctypes.c_char_p, [_I]),
 }
 
@@ -131,6 +134,16 @@ def fa_fwd_splitkv(q, k, v, o, lse, ws, B, H, Nq, Nk, d, dtype, scale, causal,
                    n_splits, stream) -> int:
     return lib().fa_fwd_splitkv(q, k, v, o, lse, ws, B, H, Nq, Nk, d, dtype,
                                 scale, causal, n_splits, stream)
+
+
+def fa_blocksparse_workspace_size(B, H, N, d, mask_per_batch) -> int:
+    return lib().fa_blocksparse_workspace_size(B, H, N, d, mask_per_batch)
+
+
+def fa_fwd_blocksparse(q, k, v, o, lse, mask, per_batch, ws, B, H, N, d, dtype,
+                       scale, causal, stream) -> int:
+    return lib().fa_fwd_blocksparse(q, k, v, o, lse, mask, per_batch, ws, B, H,
+                                    N, d, dtype, scale, causal, stream)
 
 
 # ------------------------------------------------------------ tensor helpers
@@ -359,4 +372,47 @@ def fwd_splitkv(q, k, v, n_splits: int, causal: bool = False,
                           out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
                           B, H, Nq, Nk, d, dt, float(scale), int(bool(causal)),
                           int(n_splits), _stream(q)))
+    return out, lse
+
+
+SPARSE_BLOCK = 128
+
+
+def fwd_blocksparse(q, k, v, block_mask, causal: bool = False,
+                    scale: float | None = None, out=None, lse=None,
+                    workspace=None):
+    """Block-sparse attention of [B, H, N, d] bf16/fp16 device tensors:
+    block_mask is a uint8 (or bool) device tensor [H, nb, nb] (shared by the
+    batch) or [B, H, nb, nb], nb = ceil(N / 128); nonzero = the 128-row
+    query block attends to the 128-key block."""
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(t, name, (B, H, N, d), q.dtype)
+    nb = -(-N // SPARSE_BLOCK)
+    if block_mask.dtype == torch.bool:
+        block_mask = block_mask.to(torch.uint8)
+    per_batch = 1 if block_mask.dim() == 4 else 0
+    shape = (B, H, nb, nb) if per_batch else (H, nb, nb)
+    _check_tensor(block_mask, "block_mask", shape, torch.uint8)
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor(out, "out", (B, H, N, d), q.dtype)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_tensor(lse, "lse", (B, H, N), torch.float32)
+    need = fa_blocksparse_workspace_size(B, H, N, d, per_batch)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    _check(fa_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              out.data_ptr(), lse.data_ptr(), block_mask.data_ptr(),
+                              per_batch, workspace.data_ptr(), B, H, N, d, dt,
+                              float(scale), int(bool(causal)), _stream(q)))
     return out, lse

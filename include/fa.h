@@ -212,6 +212,32 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
                    int d, int dtype, float scale, int causal, int n_splits,
                    void* stream);
 
+/*
+ * fa_fwd_blocksparse -- block-sparse attention: exact attention restricted
+ * by a block mask ("FlashAttention: Fast and Memory-Efficient Exact
+ * Attention with IO-Awareness", abstract: the extension to block-sparse
+ * attention).  The N x N score matrix is cut into blocks of 128 query rows
+ * by 128 keys; query row i may attend to key j only when
+ * block_mask[i / 128][j / 128] is nonzero (and, when causal, j <= i).  Key
+ * tiles of blocks no query row of a workgroup attends to are skipped; the
+ * others are computed with the mask applied, so the result is the
+ * definition above up to rounding.  Rows that see no key get O = 0 and
+ * LSE = -inf.
+ *   block_mask     : uint8, nb = ceil(N / 128): [H][nb][nb] shared by the
+ *                    batch (mask_per_batch = 0) or [B][H][nb][nb] (1).
+ *   workspace      : at least fa_blocksparse_workspace_size(B, H, N, d,
+ *                    mask_per_batch) bytes, 4-byte aligned; holds the
+ *                    per-tile lists of live key tiles built from the mask
+ *                    on the stream; contents on entry ignored.
+ *   Other arguments as in fa_fwd.
+ */
+size_t fa_blocksparse_workspace_size(int B, int H, int N, int d,
+                                     int mask_per_batch);
+int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o,
+                       float* lse, const void* block_mask, int mask_per_batch,
+                       void* workspace, int B, int H, int N, int d, int dtype,
+                       float scale, int causal, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_str(int status);
 

@@ -40,6 +40,14 @@ applied across parts, which Ring Attention and Lean Attention (reference list
 of the FlashAttention-3 page) use to combine per-device and per-split
 results.  The merge is checked against the definition over all keys.
 
+Block-sparse (``attention_fwd_blockmask``): FlashAttention extends to
+block-sparse attention (IO-Awareness paper, abstract on the citation-hub
+page).  The pages give no block size or mask format; the reading taken here:
+the N x N scores are cut into blocks of `block` query rows by `block` keys and
+query i may attend to key j only where the block mask is nonzero at
+(i // block, j // block) (and j <= i when causal).  That is the same
+definition with that mask; rows that see no key get O = 0, LSE = -inf.
+
 All arrays are [B, H, N, d]; inputs of any float dtype are widened to fp64.
 """
 
@@ -51,6 +59,7 @@ import numpy as np
 
 __all__ = [
     "attention_fwd",
+    "attention_fwd_blockmask",
     "attention_fwd_positions",
     "attention_fwd_positions_rows",
     "merge_partials",
@@ -322,4 +331,42 @@ def merge_partials(o_parts, lse_parts):
     o = contrib.sum(axis=0) / np.where(empty, 1.0, wsum)[..., None]
     o[empty] = 0.0
     lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, wsum)))
+    return o, lse
+
+
+def attention_fwd_blockmask(q, k, v, block_mask, block: int = 128,
+                            causal: bool = False, scale: float | None = None,
+                            rows=None):
+    """Block-sparse attention: q, k, v [B,H,N,d]; block_mask [H,nb,nb]
+    (shared by the batch) or [B,H,nb,nb], nb = ceil(N / block), nonzero =
+    the query block attends to the key block.  Rows that see no key: O = 0,
+    LSE = -inf.  `rows` (optional) restricts the output to those query rows
+    of every head.  Returns (O [B,H,R,d], LSE [B,H,R]) in fp64."""
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = default_scale(d)
+    bm = np.asarray(block_mask) != 0
+    if bm.ndim == 3:
+        bm = np.broadcast_to(bm[None], (B,) + bm.shape)
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    cols = np.arange(N)
+    o = np.empty((B, H, len(rows), d))
+    lse = np.empty((B, H, len(rows)))
+    for b in range(B):
+        for h in range(H):
+            allowed = bm[b, h][rows[:, None] // block, cols[None, :] // block]
+            if causal:
+                allowed = allowed & (cols[None, :] <= rows[:, None])
+            s = (q[b, h, rows] @ k[b, h].T) * scale
+            s = np.where(allowed, s, -np.inf)
+            m = s.max(axis=1)
+            empty = ~np.isfinite(m)
+            m_safe = np.where(empty, 0.0, m)
+            e = np.exp(s - m_safe[:, None])
+            l = e.sum(axis=1)
+            l_safe = np.where(empty, 1.0, l)
+            o[b, h] = (e / l_safe[:, None]) @ v[b, h]
+            o[b, h][empty] = 0.0
+            lse[b, h] = np.where(empty, -np.inf, m_safe + np.log(l_safe))
     return o, lse

@@ -1,0 +1,131 @@
+"""Block-sparse parity: fa_fwd_blocksparse (HIP, through the C ABI) against
+the fp64 oracle with the block mask applied (blocks of 128 query rows x 128
+keys).
+
+Bar: as the forward -- O max-abs <= 2e-2 and RMSE <= 2e-3, LSE max-abs <=
+1e-3 -- and rows that see no key come back as exactly O = 0, LSE = -inf.
+Small shapes in full; the bench shape (B=2, H=16, N=8192, d=128) with a
+sliding-window + global-column pattern on sampled rows.
+"""
+
+import numpy as np
+import pytest
+
+from exact_tiled_attention_16_amd import inputs
+from oracle.attention import attention_fwd_blockmask
+from tests.helpers import host_round, max_abs, rmse, sample_rows, to_device
+
+pytestmark = pytest.mark.gpu
+
+O_MAX_ABS = 2e-2
+O_RMSE = 2e-3
+LSE_MAX_ABS = 1e-3
+BLK = 128
+
+
+def _fa():
+    from exact_tiled_attention_16_amd import fa
+    return fa
+
+
+def _banner(msg):
+    print(f"\n[blocksparse] {msg}", flush=True)
+
+
+def _case(B, H, N, d, workload):
+    q, k, v = inputs.qkv(B, H, N, d, workload)
+    (qt, q64), (kt, k64), (vt, v64) = (host_round(x, "bf16") for x in (q, k, v))
+    return (qt, kt, vt), (q64, k64, v64)
+
+
+def _np(t):
+    import torch
+    return t.to(torch.float64).cpu().numpy()
+
+
+def _check(o, lse, o_ref, lse_ref):
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse), empty)
+    assert np.all(o[empty] == 0.0) and np.all(np.isfinite(o))
+    assert max_abs(o, o_ref) <= O_MAX_ABS
+    assert rmse(o, o_ref) <= O_RMSE
+    if (~empty).any():
+        assert max_abs(lse[~empty], lse_ref[~empty]) <= LSE_MAX_ABS
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("N", [200, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("density,per_batch", [(0.3, False), (0.7, True)])
+def test_random_masks_match_oracle(d, N, causal, density, per_batch):
+    import torch
+    fa = _fa()
+    _banner(f"d={d} N={N} causal={causal} density={density} per_batch={per_batch}")
+    B, H = 2, 3
+    (qt, kt, vt), (q64, k64, v64) = _case(B, H, N, d, 700 + d + N)
+    nb = -(-N // BLK)
+    rng = np.random.default_rng(d + N + int(causal))
+    shape = (B, H, nb, nb) if per_batch else (H, nb, nb)
+    mask = (rng.random(shape) < density).astype(np.uint8)
+    mask.reshape(-1, nb, nb)[0, 1 % nb, :] = 0      # one query block sees nothing
+    o, lse = fa.fwd_blocksparse(to_device(qt), to_device(kt), to_device(vt),
+                                torch.from_numpy(mask).cuda(), causal=causal)
+    o_ref, lse_ref = attention_fwd_blockmask(q64, k64, v64, mask, block=BLK, causal=causal)
+    _check(_np(o), _np(lse), o_ref, lse_ref)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_all_ones_mask_equals_dense_forward(causal):
+    import torch
+    fa = _fa()
+    _banner(f"all-ones mask causal={causal}")
+    (qt, kt, vt), _ = _case(2, 4, 1500, 128, 71)
+    q, k, v = to_device(qt), to_device(kt), to_device(vt)
+    nb = -(-1500 // BLK)
+    mask = torch.ones((4, nb, nb), dtype=torch.uint8, device="cuda")
+    o1, l1 = fa.fwd(q, k, v, causal=causal)
+    o2, l2 = fa.fwd_blocksparse(q, k, v, mask, causal=causal)
+    torch.cuda.synchronize()
+    # Same tiles in the same order; the skipped work is exactly zero.
+    assert max_abs(_np(o1), _np(o2)) <= 2 ** -7
+    assert max_abs(_np(l1), _np(l2)) <= 1e-5
+
+
+def test_empty_mask_gives_empty_rows():
+    import torch
+    fa = _fa()
+    _banner("all-zero mask")
+    (qt, kt, vt), _ = _case(1, 2, 300, 64, 72)
+    mask = torch.zeros((2, 3, 3), dtype=torch.uint8, device="cuda")
+    o, lse = fa.fwd_blocksparse(to_device(qt), to_device(kt), to_device(vt), mask)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_window_pattern_full_size_sampled():
+    """B=2, H=16, N=8192, d=128: each query block attends to its own and the
+    two previous key blocks plus key block 0 (sliding window + global
+    column), causal."""
+    import torch
+    fa = _fa()
+    _banner("window pattern B=2 H=16 N=8192 d=128 causal")
+    B, H, N, d = 2, 16, 8192, 128
+    (qt, kt, vt), (q64, k64, v64) = _case(B, H, N, d, 73)
+    nb = N // BLK
+    m = np.zeros((nb, nb), np.uint8)
+    for i in range(nb):
+        m[i, max(0, i - 2):i + 1] = 1
+        m[i, 0] = 1
+    mask = np.broadcast_to(m, (H, nb, nb)).copy()
+    o, lse = fa.fwd_blocksparse(to_device(qt), to_device(kt), to_device(vt),
+                                torch.from_numpy(mask).cuda(), causal=True)
+    torch.cuda.synchronize()
+    o, lse = _np(o), _np(lse)
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        rows = sample_rows(N, seed=b * 5 + h)
+        o_ref, lse_ref = attention_fwd_blockmask(q64[b:b + 1, h:h + 1], k64[b:b + 1, h:h + 1],
+                                                 v64[b:b + 1, h:h + 1], mask[h:h + 1],
+                                                 block=BLK, causal=True, rows=rows)
+        assert max_abs(o[b, h, rows], o_ref[0, 0]) <= O_MAX_ABS
+        assert rmse(o[b, h, rows], o_ref[0, 0]) <= O_RMSE
+        assert max_abs(lse[b, h, rows], lse_ref[0, 0]) <= LSE_MAX_ABS

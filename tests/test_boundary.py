@@ -43,7 +43,8 @@ def test_header_declares_expected_entry_points():
     d = _declared()
     assert {"fa_fwd", "fa_quant_fp8", "fa_fwd_fp8", "fa_bwd",
             "fa_bwd_workspace_size", "fa_status_str", "fa_fwd_partial", "fa_merge",
-            "fa_splitkv_workspace_size", "fa_fwd_splitkv"} <= set(d)
+            "fa_splitkv_workspace_size", "fa_fwd_splitkv", "fa_fwd_blocksparse",
+            "fa_blocksparse_workspace_size"} <= set(d)
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -148,6 +149,23 @@ def test_splitkv_entry_points_reject(fa):
         a = dict(base)
         a.update(kw)
         assert fa.fa_fwd_splitkv(**a) == code, kw
+
+
+def test_blocksparse_rejects_and_workspace(fa):
+    # d=128: 256-row query tiles, 64-key tiles; list = count + tiles + 6 pad.
+    n_qt, stride = 8192 // 256, 8192 // 64 + 7
+    assert fa.fa_blocksparse_workspace_size(2, 16, 8192, 128, 0) == 16 * n_qt * stride * 4
+    assert fa.fa_blocksparse_workspace_size(2, 16, 8192, 128, 1) == 32 * n_qt * stride * 4
+    assert fa.fa_blocksparse_workspace_size(2, 16, 8192, 100, 0) == 0
+    assert fa.fa_blocksparse_workspace_size(2, 16, 8192, 128, 2) == 0
+    base = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, mask=FAKE, per_batch=0, ws=FAKE,
+                B=1, H=2, N=300, d=64, dtype=0, scale=0.1, causal=0, stream=None)
+    for kw, code in ((dict(mask=None), -1), (dict(ws=None), -1), (dict(ws=FAKE + 2), -1),
+                     (dict(per_batch=2), -1), (dict(N=0), -1), (dict(q=FAKE + 4), -1),
+                     (dict(scale=-1.0), -1), (dict(d=96), -2)):
+        a = dict(base)
+        a.update(kw)
+        assert fa.fa_fwd_blocksparse(**a) == code, kw
 
 
 def test_python_helpers_reject_bad_tensors(fa):
