@@ -22,7 +22,7 @@ reported under "next_rows" (they do not enter ``value``):
                          its own and two previous 128-key blocks and block 0
                                                  4*d*(visible pairs) flop
   splitkv_decode         fa_fwd_splitkv, B=16, H=16, one query over 16,384
-                         keys, d=128, 16 parts: HBM-bound, algorithmic bytes
+                         keys, d=128, 4 parts: HBM-bound, algorithmic bytes
                          = K and V read once (+ Q, O, LSE)
 
 Legs whose entry point is not built yet report FA_ERR_UNSUPPORTED at start-up
@@ -247,7 +247,9 @@ def build_next_rows(torch, fa, dev, fwd_inputs):
 
     # Decoding: seeded device-side N(0,1) draws (torch's generator; the values
     # do not change the work).
-    DB, DH, DNq, DNk, S = 16, 16, 1, 16384, 16
+    # 4 parts: with 256 heads that already gives more workgroups than the
+    # GPU holds at once (more parts only add merge traffic).
+    DB, DH, DNq, DNk, S = 16, 16, 1, 16384, 4
     gen = torch.Generator(device=dev)
     gen.manual_seed(1000 * WORKLOAD_ID + 7)
     qd1 = torch.randn((DB, DH, DNq, d), generator=gen, device=dev).to(torch.bfloat16)

@@ -589,6 +589,17 @@ template <> struct FwdCfg<128> { static constexpr int BN = 64, NW = 8, QB = 1, O
 #endif
 template <> struct FwdCfg<256> { static constexpr int BN = 32, NW = 4, QB = 1, OCC = 1, NSTG = 3; };
 
+// Partial (split-KV) calls with at most kNarrowRows query rows -- decoding --
+// use one wave per workgroup (32 query rows instead of 256, so far less of
+// the matrix work is padding), 32-key tiles and a two-stage ring (32 KiB of
+// LDS at d = 128), so that several workgroups share a CU: with so little
+// compute per key the kernel is bound by HBM, and independent workgroups keep
+// more K/V bytes in flight per CU than one workgroup's ring can.
+constexpr int kNarrowRows = 32;
+template <int D> struct FwdNarrowCfg {
+  static constexpr int BN = 32, NW = 1, QB = 1, OCC = D == 256 ? 1 : 2, NSTG = 2;
+};
+
 // Block-sparse list geometry per head dimension: query tiles per head and
 // ints per list (count, one entry per key tile, kSparsePad padding entries:
 // the pipeline reads up to four positions past the last live tile).
@@ -613,10 +624,10 @@ int query_resident_slots(K kernel, int threads) {
   return cus * per_cu;
 }
 
-template <int D, bool CAUSAL, bool PERSIST, bool PARTIAL, int DT, bool SPARSE = false>
+template <int D, bool CAUSAL, bool PERSIST, bool PARTIAL, int DT, bool SPARSE = false,
+          class C = FwdCfg<D>>
 hipError_t launch_one(const FwdArgs& a, int BH, hipStream_t stream,
                       const int* bs_list = nullptr) {
-  using C = FwdCfg<D>;
   constexpr int BM = 32 * C::QB * C::NW;
   FwdArgs args = a;
   args.n_qtiles = (a.N + BM - 1) / BM;
@@ -668,6 +679,11 @@ hipError_t launch_dtype(const FwdArgs& a, int BH, int d, bool causal, hipStream_
 
 template <int D, int DT>
 hipError_t launch_partial_d(const FwdArgs& a, int BH, bool causal, hipStream_t s) {
+  if (a.N <= kNarrowRows) {
+    using C = FwdNarrowCfg<D>;
+    return causal ? launch_one<D, true, false, true, DT, false, C>(a, BH, s)
+                  : launch_one<D, false, false, true, DT, false, C>(a, BH, s);
+  }
   return causal ? launch_one<D, true, false, true, DT>(a, BH, s)
                 : launch_one<D, false, false, true, DT>(a, BH, s);
 }
