@@ -164,11 +164,13 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
   // which run up to a few positions past the end, need no bounds check (a
   // branch there would break the straight-line schedule of the loop).
   const int* lst = nullptr;
-  int nlist = 0;
+  int nlist = 0, nfull = 0;
   if constexpr (SPARSE) {
     const int mh = a.bs_per_batch ? bh : bh % a.heads;
     lst = bs_list + ((int64_t)mh * a.n_qtiles + qt) * a.bs_stride;
     nlist = lst[0];
+    nfull = lst[1];  // leading live tiles that need no mask
+    lst += 1;        // entries at lst[1 + j]
   }
   auto tile_of = [&](int j) { return lst[1 + j] & 0xffffff; };
   const int ntiles = SPARSE ? nlist : (kend + BN - 1) / BN;
@@ -366,7 +368,10 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
   int t_mask = (kn % BN) ? kn / BN : ntiles;
   if (CAUSAL) t_mask = min(t_mask, max(q0 + coff + 1, 0) / BN);
   t_mask = min(t_mask, ntiles);
-  if constexpr (SPARSE) t_mask = 0;  // every listed tile may be masked for some wave
+  // Block-sparse: tiles dead for some wave of a multi-block workgroup need
+  // the masked body; with one query block per workgroup only the trailing
+  // diagonal / ragged tiles do.
+  if constexpr (SPARSE) t_mask = BM > kSparseBlock ? 0 : nfull;
 
   Scores sA, sB;
   Probs pA, pB;
@@ -451,7 +456,8 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
       const int t = SPARSE ? tile_of(j + 1) : j + 1;
       // Block-sparse: the wave's query block does not attend to this tile.
       bool dead = false;
-      if constexpr (SPARSE) dead = !((lst[2 + j] >> (24 + (wave * WQ) / 128)) & 1);
+      if constexpr (SPARSE && BM > kSparseBlock)
+        dead = !((lst[2 + j] >> (24 + (wave * WQ) / kSparseBlock)) & 1);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         int lim = kn - t * BN - 4 * hl;
@@ -601,17 +607,27 @@ template <int D> struct FwdNarrowCfg {
 };
 
 // Block-sparse list geometry per head dimension: query tiles per head and
-// ints per list (count, one entry per key tile, kSparsePad padding entries:
-// the pipeline reads up to four positions past the last live tile).
+// ints per list (count, unmasked count, one entry per key tile, kSparsePad
+// padding entries: the pipeline reads up to four positions past the last
+// live tile).
 constexpr int kSparsePad = 6;
+// Block-sparse launches use workgroups of one 128-row query block (four
+// waves), so a workgroup computes exactly its block's live key tiles, and a
+// two-stage ring at d <= 128 so that two workgroups share a CU (a sparse
+// workgroup has few tiles; its prologue and epilogue overlap the other's).
+template <int D> struct FwdSparseCfg {
+  static constexpr int BN = D == 256 ? 32 : 64, NW = 4, QB = 1, OCC = D == 256 ? 1 : 2,
+                       NSTG = D == 256 ? 3 : 2;
+};
+
 template <int D>
 int sparse_qtiles(int N) {
-  constexpr int BM = 32 * FwdCfg<D>::QB * FwdCfg<D>::NW;
+  constexpr int BM = 32 * FwdSparseCfg<D>::QB * FwdSparseCfg<D>::NW;
   return (N + BM - 1) / BM;
 }
 template <int D>
 int sparse_list_stride(int N) {
-  return (N + FwdCfg<D>::BN - 1) / FwdCfg<D>::BN + 1 + kSparsePad;
+  return (N + FwdSparseCfg<D>::BN - 1) / FwdSparseCfg<D>::BN + 2 + kSparsePad;
 }
 
 // Workgroups of `kernel` resident at once on the current device.
@@ -699,16 +715,17 @@ hipError_t launch_partial_dtype(const FwdArgs& a, int BH, int d, bool causal, hi
 }
 
 // Live key tiles of each (mask head, query tile) of the block-sparse forward:
-// out[0] = count, out[1 + i] = key tile | (query-block bits << 24), in
-// increasing tile order, then kSparsePad entries naming the first tile past
-// the last key with no bits.  A key tile is live when some 128-row query block of
+// out[0] = count, out[1] = how many leading entries need no mask (full tiles
+// below the causal diagonal of every row of the tile), out[2 + i] = key tile |
+// (query-block bits << 24), in increasing tile order, then kSparsePad
+// entries naming the first tile past the last key with no bits.  A key tile is live when some 128-row query block of
 // the workgroup's tile attends to its 128-key block (and, when causal, the
 // tile is not wholly above the diagonal).  One thread per list.
 template <int D>
 __global__ void __launch_bounds__(256)
 bs_index_kernel(const uint8_t* __restrict__ mask, int* __restrict__ out, int n_lists,
                 int n_qtiles, int N, int stride, int causal) {
-  using C = FwdCfg<D>;
+  using C = FwdSparseCfg<D>;
   constexpr int BM = 32 * C::QB * C::NW;
   constexpr int BN = C::BN;
   constexpr int QBW = BM / kSparseBlock;  // query blocks per workgroup tile
@@ -722,8 +739,11 @@ bs_index_kernel(const uint8_t* __restrict__ mask, int* __restrict__ out, int n_l
   const int q0 = qt * BM;
   const int qlast = min(q0 + BM, N) - 1;
   const uint8_t* mrow = mask + (int64_t)mh * nb * nb;
-  int* o = out + gid * stride;
-  int count = 0;
+  int* o = out + gid * stride + 1;
+  int count = 0, full = 0;
+  // Tiles below this need no mask: every key of the tile exists and is at or
+  // before every query row of the workgroup tile.
+  const int t_nomask = min(N / BN, causal ? (q0 + 1) / BN : N / BN);
   for (int t = 0; t < nkt; ++t) {
     if (causal && t * BN > qlast) break;
     const int kb = t * BN / kSparseBlock;
@@ -733,16 +753,20 @@ bs_index_kernel(const uint8_t* __restrict__ mask, int* __restrict__ out, int n_l
       const int qblk = q0 / kSparseBlock + b;
       if (qblk < nb && mrow[(int64_t)qblk * nb + kb] != 0) bits |= 1 << b;
     }
-    if (bits) o[1 + count++] = t | (bits << 24);
+    if (bits) {
+      if (full == count && t < t_nomask && bits == (1 << QBW) - 1) full = count + 1;
+      o[1 + count++] = t | (bits << 24);
+    }
   }
   for (int i = 0; i < kSparsePad; ++i) o[1 + count + i] = nkt;
-  o[0] = count;
+  out[gid * stride] = count;
+  o[0] = full;
 }
 
 template <int D, int DT>
 hipError_t launch_sparse_d(const FwdArgs& a, int BH, bool causal, const uint8_t* mask,
                            int* list, hipStream_t s) {
-  using C = FwdCfg<D>;
+  using C = FwdSparseCfg<D>;
   constexpr int BM = 32 * C::QB * C::NW;
   FwdArgs args = a;
   const int n_qtiles = (a.N + BM - 1) / BM;
@@ -754,8 +778,8 @@ hipError_t launch_sparse_d(const FwdArgs& a, int BH, bool causal, const uint8_t*
                      (int)n_lists, n_qtiles, a.N, args.bs_stride, causal ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return causal ? launch_one<D, true, false, false, DT, true>(args, BH, s, list)
-                : launch_one<D, false, false, false, DT, true>(args, BH, s, list);
+  return causal ? launch_one<D, true, false, false, DT, true, C>(args, BH, s, list)
+                : launch_one<D, false, false, false, DT, true, C>(args, BH, s, list);
 }
 
 template <int DT>

@@ -152,8 +152,8 @@ def test_splitkv_entry_points_reject(fa):
 
 
 def test_blocksparse_rejects_and_workspace(fa):
-    # d=128: 256-row query tiles, 64-key tiles; list = count + tiles + 6 pad.
-    n_qt, stride = 8192 // 256, 8192 // 64 + 7
+    # d=128: 128-row query tiles, 64-key tiles; list = 2 counts + tiles + 6 pad.
+    n_qt, stride = 8192 // 128, 8192 // 64 + 8
     assert fa.fa_blocksparse_workspace_size(2, 16, 8192, 128, 0) == 16 * n_qt * stride * 4
     assert fa.fa_blocksparse_workspace_size(2, 16, 8192, 128, 1) == 32 * n_qt * stride * 4
     assert fa.fa_blocksparse_workspace_size(2, 16, 8192, 100, 0) == 0
