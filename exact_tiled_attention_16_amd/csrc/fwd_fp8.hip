@@ -28,6 +28,11 @@
 #include "common.h"
 #include "kernels.h"
 
+// Operand fragments read ahead of the fp8 matrix instructions.
+#ifndef FA_FP8_PF
+#define FA_FP8_PF 2
+#endif
+
 namespace fa {
 
 namespace {
@@ -276,14 +281,21 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   constexpr int NS_S = NKB * NDC, NS_PV = NDB;
   constexpr int NSTEP = (NS_S + NS_PV) / 2;
   static_assert((NS_S + NS_PV) % 2 == 0, "two matrix instructions per step");
+  // The K and V scales of tile j are loaded one iteration ahead: a scalar
+  // load shares its wait counter with the LDS reads, so waiting for it inside
+  // the steps would also wait for every fragment read in flight.
+  float ks_pre = kscale(-1), vs_pre = vscale(-1);
   auto fused = [&](auto ds_tag, auto ms_tag, auto dp_tag, auto dpv_tag, int j, int st,
                    const Scores& s_cur, Scores& s_nxt, Probs& p_cur, const Probs& p_prev) {
     constexpr bool DS = decltype(ds_tag)::value, MS = decltype(ms_tag)::value;
     constexpr bool DP = decltype(dp_tag)::value, DPV = decltype(dpv_tag)::value;
+    const float ks_j = ks_pre, vs_j = vs_pre;
+    ks_pre = kscale(j + 1);
+    vs_pre = vscale(j + 1);
     issue_iter(j, st);
     const FA_LDS uint8_t* ks = lds + snext(st) * TILEB;
     const FA_LDS uint8_t* vs = lds + (NSTG + sprev(st)) * TILEB;
-    const float mul = qmul * kscale(j);  // tile j's scores to log2 units
+    const float mul = qmul * ks_j;  // tile j's scores to log2 units
     const float m_neg = -m_run;
     if constexpr (DS) {
 #pragma unroll
@@ -297,18 +309,31 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
     // needed before the next iteration.
     const i32x8_t pf = {p_prev[0], p_prev[1], p_prev[2], p_prev[3],
                         p_prev[4], p_prev[5], p_prev[6], p_prev[7]};
+    // Matrix instructions m = M0 .. M1-1 of this iteration (PV first, then
+    // S); the operand fragment of instruction m is read PF instructions
+    // ahead, into a ring of PF + 1 fragments.
+    constexpr int M0 = DPV ? 0 : NS_PV, M1 = DS ? NS_PV + NS_S : NS_PV;
+    constexpr int PF = FA_FP8_PF;
+    auto frag = [&](int m) {
+      if (m < NS_PV) return ld_v(vs, m);
+      return ld_k(ks, (m - NS_PV) / NDC, (m - NS_PV) % NDC);
+    };
+    i32x8_t fr[PF + 1];
+#pragma unroll
+    for (int m = M0; m < M1 && m < M0 + PF; ++m) fr[(m - M0) % (PF + 1)] = frag(m);
 #pragma unroll
     for (int step = 0; step < NSTEP; ++step) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int m = 2 * step + u;  // matrix instruction index: PV first, then S
-        if constexpr (DPV) {
-          if (m < NS_PV) oacc[m] = mfma_fp8(ld_v(vs, m), pf, oacc[m]);
-        }
-        if constexpr (DS) {
-          if (m >= NS_PV && m - NS_PV < NS_S) {
+        if (m >= M0 && m < M1) {
+          if (m + PF < M1) fr[(m + PF - M0) % (PF + 1)] = frag(m + PF);
+          const i32x8_t& f = fr[(m - M0) % (PF + 1)];
+          if (m < NS_PV) {
+            oacc[m] = mfma_fp8(f, pf, oacc[m]);
+          } else {
             const int kb = (m - NS_PV) / NDC, dc = (m - NS_PV) % NDC;
-            s_nxt[kb] = mfma_fp8(ld_k(ks, kb, dc), qf[dc], s_nxt[kb]);
+            s_nxt[kb] = mfma_fp8(f, qf[dc], s_nxt[kb]);
           }
         }
       }
@@ -342,7 +367,7 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
         for (int r = 0; r < 16; ++r)
           if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s_nxt[kb][r] = -INFINITY;
     }
-    if constexpr (DP) finish_tile(s_cur, p_cur, mul, ps0 + ps1, vscale(j));
+    if constexpr (DP) finish_tile(s_cur, p_cur, mul, ps0 + ps1, vs_j);
     dma_sync<2 * IPW>();
   };
   using T_ = std::true_type;
