@@ -53,11 +53,6 @@ template <> struct Elem<0> {
     f32x2_t v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
   }
-  // acc + lo + hi of a packed pair (one v_dot2 against (1, 1)).
-  static __device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
-    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair), one, acc, false);
-  }
 };
 
 template <> struct Elem<1> {
@@ -68,10 +63,6 @@ template <> struct Elem<1> {
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     f32x2_t v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
-  }
-  static __device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
-    const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pair), one, acc, false);
   }
 };
 
@@ -97,27 +88,18 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // True in every lane when the predicate holds in at least one lane.
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
-// The running row maximum used as the exp2 reference is only raised when a
-// tile's maximum exceeds it by more than this many log2 units.  Probabilities
-// are then at most 2^kLazyMax and the output / normaliser rescale is skipped
-// for most tiles; O and l share the same reference, so the result is exact.
-constexpr float kLazyMax = 8.0f;
-
-// Variant keyed on the probabilities themselves: the reference is raised when
-// one lane's partial row sum of a tile's probabilities (computed against the
-// current reference) exceeds kLazySum, or is not finite.  Below the bound every
-// probability is at most kLazySum, and the reference never exceeds the running
-// maximum, so it stays exact and needs no per-tile maximum.
+// Lazy softmax reference: the running row maximum used as the exp2 reference
+// is raised only when one lane's partial row sum of a tile's probabilities
+// (computed against the current reference) exceeds kLazySum, or is not
+// finite.  Below the bound every probability is at most kLazySum, and the
+// reference never exceeds the running maximum, so the result stays exact and
+// needs no per-tile maximum.
 constexpr float kLazySum = 1024.0f;
 
 // ---------------------------------------------------------------- memory
 
 __device__ __forceinline__ u32x4_t ld_global16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
-}
-
-__device__ __forceinline__ void st_lds16(FA_LDS void* p, u32x4_t v) {
-  *reinterpret_cast<FA_LDS u32x4_t*>(p) = v;
 }
 
 __device__ __forceinline__ u32x4_t ld_lds16(const FA_LDS void* p) {
@@ -127,15 +109,6 @@ __device__ __forceinline__ u32x4_t ld_lds16(const FA_LDS void* p) {
 __device__ __forceinline__ s16x4_t ld_lds_tr16(const FA_LDS void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       reinterpret_cast<FA_LDS s16x4_t*>(const_cast<FA_LDS void*>(p)));
-}
-
-// Asynchronous global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
-// lane i writes bytes [16 i, 16 i + 16) of the 1 KiB block at `lds_block`,
-// which must be the same for the whole wave.  Completion is tracked by the
-// vector-memory counter, not by the LDS counter.
-__device__ __forceinline__ void dma16(const void* src, FA_LDS void* lds_block) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (FA_LDS void*)lds_block, 16, 0, 0);
 }
 
 // Buffer resource for `bytes` bytes at `base` (wave-uniform): base address in

@@ -32,9 +32,9 @@ def _banner(msg):
     print(f"\n[blocksparse] {msg}", flush=True)
 
 
-def _case(B, H, N, d, workload):
+def _case(B, H, N, d, workload, dtype="bf16"):
     q, k, v = inputs.qkv(B, H, N, d, workload)
-    (qt, q64), (kt, k64), (vt, v64) = (host_round(x, "bf16") for x in (q, k, v))
+    (qt, q64), (kt, k64), (vt, v64) = (host_round(x, dtype) for x in (q, k, v))
     return (qt, kt, vt), (q64, k64, v64)
 
 
@@ -71,6 +71,21 @@ def test_random_masks_match_oracle(d, N, causal, density, per_batch):
     o, lse = fa.fwd_blocksparse(to_device(qt), to_device(kt), to_device(vt),
                                 torch.from_numpy(mask).cuda(), causal=causal)
     o_ref, lse_ref = attention_fwd_blockmask(q64, k64, v64, mask, block=BLK, causal=causal)
+    _check(_np(o), _np(lse), o_ref, lse_ref)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_fp16_random_mask(d):
+    import torch
+    fa = _fa()
+    _banner(f"fp16 d={d}")
+    B, H, N = 1, 2, 700
+    (qt, kt, vt), (q64, k64, v64) = _case(B, H, N, d, 740 + d, "fp16")
+    nb = -(-N // BLK)
+    mask = (np.random.default_rng(d).random((H, nb, nb)) < 0.5).astype(np.uint8)
+    o, lse = fa.fwd_blocksparse(to_device(qt), to_device(kt), to_device(vt),
+                                torch.from_numpy(mask).cuda(), causal=True)
+    o_ref, lse_ref = attention_fwd_blockmask(q64, k64, v64, mask, block=BLK, causal=True)
     _check(_np(o), _np(lse), o_ref, lse_ref)
 
 

@@ -126,6 +126,19 @@ def test_splitkv_matches_oracle(B, H, Nq, Nk, d, splits, causal):
     _compare(_np(o), _np(lse), o_ref, lse_ref, "splitkv")
 
 
+@pytest.mark.parametrize("Nq,splits", [(1, 8), (40, 3)])
+def test_splitkv_fp16(Nq, splits):
+    """fp16 inputs through both partial configurations (one-wave workgroups
+    for Nq <= 32, the default tile otherwise) and the fp16 merge."""
+    fa = _fa()
+    _banner(f"splitkv fp16 Nq={Nq} splits={splits}")
+    B, H, Nk, d = 2, 3, 777, 128
+    (qt, kt, vt), (q64, k64, v64) = _inputs(B, H, Nq, Nk, d, 450 + Nq, dtype="fp16")
+    o, lse = fa.fwd_splitkv(to_device(qt), to_device(kt), to_device(vt), splits, causal=True)
+    o_ref, lse_ref = attention_fwd_positions(q64, k64, v64, causal=True, q_pos0=Nk - Nq)
+    _compare(_np(o), _np(lse), o_ref, lse_ref, "splitkv fp16")
+
+
 def test_splitkv_equal_lengths_matches_fa_fwd():
     """With Nq = Nk the split result equals the single-pass forward to within
     rounding (the parts change only the order of the fp32 sums)."""
