@@ -157,7 +157,8 @@ def build_legs(torch, fa, dev):
     # (and its roofline reported) as that one launch sequence.
     legs.append(dict(name="bwd_bf16", call=bwd_call, flops=2.5 * fwd_flops(B, H, N, d),
                      dtype="bf16", kernel="bwd_pre_kernel+bwd_kv2_kernel+bwd_dq_kernel"))
-    return legs, (qd, kd, vd)
+    outputs = {"fwd_bf16": (o, lse), "fwd_fp8": (o8,), "bwd_bf16": (dq, dk, dv)}
+    return legs, (qd, kd, vd), outputs
 
 
 def build_next_rows(torch, fa, dev, fwd_inputs):
@@ -325,10 +326,27 @@ def time_next_rows(torch, fa, rows, steps, warmup, rounds=5):
     return report
 
 
-def cpu_baseline(legs_present, budget_s=15.0):
+def shader_clock():
+    """Current shader clock as rocm-smi reports it (MHz), or None."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
+                           timeout=20)
+        m = re.search(r"sclk[^\n]*?\((\d+)\s*Mhz\)", r.stdout, re.I)
+        return int(m.group(1)) if m else None
+    except Exception:
+        return None
+
+
+def cpu_baseline(legs_present, budget_s=15.0, gpu_out=None):
     """Time the fp64 oracle on the host on a bounded sample of the same
-    workload: the first heads of batch 0, one at a time, until ~budget_s."""
+    workload: the first heads of batch 0, one at a time, until ~budget_s.
+    The oracle runs on the values the GPU legs consumed (the bf16 rounding of
+    the same seeded draws), so its results also check the timed GPU outputs
+    of those heads (gpu_out: batch 0 of each leg's outputs, after timing)."""
     import numpy as np
+    import torch
     from exact_tiled_attention_16_amd import inputs
     from oracle import attention as oatt
     from oracle import fp8 as ofp8
@@ -338,8 +356,15 @@ def cpu_baseline(legs_present, budget_s=15.0):
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
     B, H, N, d = (WORKLOAD[k] for k in "BHNd")
-    q, k, v = inputs.qkv(1, H, N, d, WORKLOAD_ID)
-    do = inputs.dout(1, H, N, d, WORKLOAD_ID)
+    def bf16(x):
+        return torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    q, k, v = (bf16(x) for x in inputs.qkv(1, H, N, d, WORKLOAD_ID))
+    do = bf16(inputs.dout(1, H, N, d, WORKLOAD_ID))
+    gpu_out = gpu_out or {}
+    err = {}
+
+    def note(key, value):
+        err[key] = max(err.get(key, 0.0), float(value))
     s = inputs.signs(d, WORKLOAD_ID)
     flops = 0.0
     heads = 0
@@ -347,22 +372,42 @@ def cpu_baseline(legs_present, budget_s=15.0):
     while heads < H and time.perf_counter() - t0 < budget_s:
         sl = (slice(0, 1), slice(heads, heads + 1))
         qh, kh, vh, doh = q[sl], k[sl], v[sl], do[sl]
+        h = heads
         if "fwd_bf16" in legs_present:
-            oatt.attention_fwd(qh, kh, vh)
+            o_ref, lse_ref = oatt.attention_fwd(qh, kh, vh)
             flops += fwd_flops(1, 1, N, d)
+            if "fwd_bf16" in gpu_out:
+                note("fwd_bf16_o_max_abs", np.abs(gpu_out["fwd_bf16"][0][h] - o_ref[0, 0]).max())
+                note("fwd_bf16_lse_max_abs",
+                     np.abs(gpu_out["fwd_bf16"][1][h] - lse_ref[0, 0]).max())
         if "fwd_fp8" in legs_present:
             q8, qs = ofp8.quantize_fp8(qh, signs=s, scale_mul=1.0 / d)
             k8, ks = ofp8.quantize_fp8(kh, signs=s)
             v8, vs = ofp8.quantize_fp8(vh)
             ofp8.attention_fwd_fp8(q8, k8, v8, qs, ks, vs)
             flops += fwd_flops(1, 1, N, d)
+            if "fwd_fp8" in gpu_out and "fwd_bf16" in legs_present:
+                # Error of the fp8 path against exact attention (what the
+                # fp8 leg is measured by).
+                note("fwd_fp8_o_rmse_vs_exact",
+                     np.sqrt(np.mean((gpu_out["fwd_fp8"][0][h] - o_ref[0, 0]) ** 2)))
         if "bwd_bf16" in legs_present:
-            oatt.attention_bwd(qh, kh, vh, doh)
+            grads = oatt.attention_bwd(qh, kh, vh, doh)
             flops += 2.5 * fwd_flops(1, 1, N, d)
+            if "bwd_bf16" in gpu_out:
+                for name, g, ref in zip(("dq", "dk", "dv"), gpu_out["bwd_bf16"], grads):
+                    note(f"bwd_{name}_rel_frobenius",
+                         np.linalg.norm(g[h] - ref[0, 0]) / np.linalg.norm(ref[0, 0]))
         heads += 1
     dt = time.perf_counter() - t0
+    verify = None
+    if err:
+        ok = (err.get("fwd_bf16_o_max_abs", 0) <= 2e-2 and err.get("fwd_bf16_lse_max_abs", 0) <= 1e-3
+              and all(v <= 1e-2 for key, v in err.items() if key.endswith("rel_frobenius")))
+        verify = {"heads": heads, "pass": bool(ok),
+                  **{key: float(f"{v:.3e}") for key, v in err.items()}}
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "verify_timed_outputs": verify,
             "sample": f"fp64 numpy oracle, legs {sorted(legs_present)}, {heads} of "
                       f"{B * H} heads (b=0, h<{heads}) of B={B},H={H},N={N},d={d}, "
                       f"{dt:.1f} s wall"}
@@ -395,7 +440,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     fa.lib()
-    legs_all, fwd_inputs = build_legs(torch, fa, dev)
+    legs_all, fwd_inputs, leg_outputs = build_legs(torch, fa, dev)
     torch.cuda.synchronize()
 
     # Keep the legs whose entry point is built; any other failure is fatal.
@@ -431,6 +476,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    clock_before = shader_clock()
 
     # Timed region: exactly --steps steps between two synchronisations.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -447,9 +493,10 @@ def main():
     for _ in range(args.steps):
         step(events)
     torch.cuda.synchronize()
-    leg_ms = {n: sum(a.elapsed_time(b) for a, b in zip(*ev)) / len(ev[0])
-              for n, ev in events.items()}
+    leg_times = {n: sorted(a.elapsed_time(b) for a, b in zip(*ev)) for n, ev in events.items()}
+    leg_ms = {n: sum(t) / len(t) for n, t in leg_times.items()}
 
+    clock_after = shader_clock()
     next_rows = None
     if not args.no_next_rows:
         next_rows = time_next_rows(torch, fa, build_next_rows(torch, fa, dev, fwd_inputs),
@@ -469,8 +516,11 @@ def main():
     for l in legs:
         ms = leg_ms[l["name"]]
         tf = l["flops"] / (ms * 1e-3) / 1e12 if l["flops"] else None
+        ts = leg_times[l["name"]]
         leg_report[l["name"]] = {
             "ms": round(ms, 4),
+            "ms_median": round(ts[len(ts) // 2], 4),
+            "ms_best": round(ts[0], 4),
             "tflops": round(tf, 2) if tf else None,
             "frac_of_peak": round(tf / PEAK_TFLOPS[l["dtype"]], 4) if tf else None,
         }
@@ -506,10 +556,14 @@ def main():
         "legs": leg_report,
         "roofline": roofline,
     }
+    out["clock"] = {"before": clock_before, "after": clock_after,
+                    "source": "rocm-smi --showclocks (current sclk), best effort"}
     if next_rows is not None:
         out["next_rows"] = next_rows
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline({l["name"] for l in legs}, args.cpu_budget)
+        host_out = {n: tuple(t[0].float().cpu().numpy() for t in ts)
+                    for n, ts in leg_outputs.items() if n in {l["name"] for l in legs}}
+        out["cpu_baseline"] = cpu_baseline({l["name"] for l in legs}, args.cpu_budget, host_out)
     print(json.dumps(out), flush=True)
 
 
