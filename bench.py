@@ -326,6 +326,41 @@ def time_next_rows(torch, fa, rows, steps, warmup, rounds=5):
     return report
 
 
+def clock_under_load(torch, call, ms_per_call, dev, n_min=20):
+    """Shader clock while `call` runs back to back: a one-wave probe kernel
+    (libfa_probe.so) on a second stream (default priority) sleeps through
+    about 80 % of the launches and reads the shader-cycle counter and the
+    wall clock at both ends.  Returns MHz, or None if the probe library is
+    missing."""
+    import ctypes
+    path = os.path.join(ROOT, "exact_tiled_attention_16_amd", "libfa_probe.so")
+    if not os.path.exists(path):
+        return None
+    probe = ctypes.CDLL(path)
+    probe.fa_probe_clock.restype = ctypes.c_int
+    probe.fa_probe_clock.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p]
+    probe.fa_probe_wall_rate_khz.restype = ctypes.c_longlong
+    rate_khz = probe.fa_probe_wall_rate_khz()
+    if rate_khz <= 0:
+        return None
+    out = torch.zeros(4, dtype=torch.int64, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    n = max(n_min, int(math.ceil(20.0 / max(ms_per_call, 1e-3))))  # >= 20 ms of work
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    ticks = int(0.8 * n * ms_per_call * rate_khz)
+    if probe.fa_probe_clock(out.data_ptr(), ticks, side.cuda_stream) != 0:
+        return None
+    for _ in range(n):
+        call()
+    torch.cuda.synchronize()
+    w0, w1, c0, c1 = (int(x) for x in out.cpu())
+    if w1 <= w0:
+        return None
+    return round((c1 - c0) / ((w1 - w0) / (rate_khz * 1e3)) / 1e6)
+
+
 def shader_clock():
     """Current shader clock as rocm-smi reports it (MHz), or None."""
     import re
@@ -497,6 +532,10 @@ def main():
     leg_ms = {n: sum(t) / len(t) for n, t in leg_times.items()}
 
     clock_after = shader_clock()
+    # Shader clock while each leg runs alone (the power draw, hence the clock,
+    # differs between legs).
+    leg_clock = {l["name"]: clock_under_load(torch, l["call"], leg_ms[l["name"]], dev)
+                 for l in legs}
     next_rows = None
     if not args.no_next_rows:
         next_rows = time_next_rows(torch, fa, build_next_rows(torch, fa, dev, fwd_inputs),
@@ -517,10 +556,14 @@ def main():
         ms = leg_ms[l["name"]]
         tf = l["flops"] / (ms * 1e-3) / 1e12 if l["flops"] else None
         ts = leg_times[l["name"]]
+        clk = leg_clock.get(l["name"])
         leg_report[l["name"]] = {
             "ms": round(ms, 4),
             "ms_median": round(ts[len(ts) // 2], 4),
             "ms_best": round(ts[0], 4),
+            "clock_mhz": clk,
+            "frac_of_peak_at_clock": (round(tf / (PEAK_TFLOPS[l["dtype"]] * clk / 2400.0), 4)
+                                      if tf and clk else None),
             "tflops": round(tf, 2) if tf else None,
             "frac_of_peak": round(tf / PEAK_TFLOPS[l["dtype"]], 4) if tf else None,
         }
@@ -556,8 +599,17 @@ def main():
         "legs": leg_report,
         "roofline": roofline,
     }
-    out["clock"] = {"before": clock_before, "after": clock_after,
-                    "source": "rocm-smi --showclocks (current sclk), best effort"}
+    out["clock"] = {"idle_mhz_before": clock_before, "idle_mhz_after": clock_after,
+                    "source": "idle: rocm-smi --showclocks (current sclk), best effort; per "
+                              "leg (legs.*.clock_mhz): shader-cycle and wall-clock counters "
+                              "read by a one-wave probe kernel while the leg runs back to back"}
+    dom_clk = leg_clock.get(dom["name"])
+    if dom_clk:
+        # The spec peaks assume 2.4 GHz; the fraction of the peak at the
+        # clock the chip actually ran at, for context.
+        roofline["clock_mhz"] = dom_clk
+        roofline["frac_at_measured_clock"] = round(achieved / (PEAK_TFLOPS[dom["dtype"]] *
+                                                               dom_clk / 2400.0), 4)
     if next_rows is not None:
         out["next_rows"] = next_rows
     if not args.no_cpu_baseline:

@@ -2,7 +2,8 @@
 
 ``python -m exact_tiled_attention_16_amd.build`` (or ``build()``) compiles
 every translation unit under ``csrc/`` to an object in ``_build/`` at the
-repository root and links ``exact_tiled_attention_16_amd/libfa.so``.  It always
+repository root and links ``exact_tiled_attention_16_amd/libfa.so`` (and the
+clock probe used by bench.py, ``libfa_probe.so``).  It always
 recompiles; loading code never builds.
 """
 
@@ -20,6 +21,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
+# Measurement aid used by bench.py (shader clock under load); not part of the
+# attention library.
+PROBE_SOURCE = "clock_probe.hip"
+PROBE_LIB = os.path.join(PKG, "libfa_probe.so")
 
 ARCH = "gfx950"
 SOURCES = ["fa_api.cpp", "fwd.hip", "bwd.hip", "quant.hip", "fwd_fp8.hip", "merge.hip"]
@@ -62,19 +67,23 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs,
-           "-o", tmp]
+def _link(objs, out, verbose):
+    tmp = out + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + [PROBE_SOURCE]))
+    _link([os.path.join(OBJDIR, os.path.splitext(PROBE_SOURCE)[0] + ".o")], PROBE_LIB, verbose)
+    _link(objs[:len(SOURCES)], LIB, verbose)
     return LIB
 
 

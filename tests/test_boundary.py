@@ -175,3 +175,17 @@ def test_python_helpers_reject_bad_tensors(fa):
         fa.fwd(q, q, q)  # host tensors are refused before any call
     with pytest.raises(ValueError):
         fa.fwd(torch.zeros(8, 64, dtype=torch.bfloat16), q, q)
+
+
+def test_clock_probe_library_exports():
+    """The bench's clock probe is its own small library (not the C ABI of the
+    attention library); it must be built and export its two entry points."""
+    import ctypes
+    path = os.path.join(ROOT, "exact_tiled_attention_16_amd", "libfa_probe.so")
+    if not os.path.exists(path):
+        pytest.fail("libfa_probe.so is not built; run `python -m exact_tiled_attention_16_amd.build`")
+    lib = ctypes.CDLL(path)
+    assert hasattr(lib, "fa_probe_clock") and hasattr(lib, "fa_probe_wall_rate_khz")
+    lib.fa_probe_clock.restype = ctypes.c_int
+    lib.fa_probe_clock.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p]
+    assert lib.fa_probe_clock(None, 100, None) == -1  # rejected before any launch
