@@ -11,19 +11,20 @@
 // Kernels:
 //   bwd_pre_kernel  per query row: -LSE / scale and -D into two planes of the
 //                   workspace (all rows of one, then all rows of the other).
-//   bwd_kv2_kernel  one workgroup of 8 waves per (b, h, tile of 128 keys); the
+//   bwd_kv3_kernel  one workgroup of 8 waves per (b, h, tile of 128 keys); the
 //                   four 32-key blocks each get two waves that share a SIMD:
 //                   one keeps the block's K rows and dV accumulator (S, P,
 //                   dV^T += dO^T P), the other its V rows and dK accumulator
-//                   (dP, dS = P o (dP - D), dK^T += Q^T dS); P passes between
-//                   them through LDS in fp32.  Query tiles of 64 rows (Q, dO,
-//                   row statistics) stream through a three-stage LDS ring
-//                   filled by buffer loads with an LDS destination.  Keys are
-//                   accumulator columns (one key per lane); Q and dO are read
-//                   from LDS as rows (S, dP) and by transposed 16-bit reads
-//                   (dV, dK).  The S and dP accumulators start from the row
-//                   statistics, and dK = scale * dS^T Q is scaled once at the
-//                   end.
+//                   (dP, dS = P o (dP - D), dK^T += Q^T dS, one tile late); P
+//                   passes between them through two LDS buffers in the input
+//                   type.  Query tiles of 64 rows (Q, dO, row statistics)
+//                   stream through a three-stage LDS ring filled by buffer
+//                   loads with an LDS destination; one barrier per tile.  Keys
+//                   are accumulator columns (one key per lane); Q and dO are
+//                   read from LDS as rows (S, dP) and by transposed 16-bit
+//                   reads (dV, dK).  The S and dP accumulators start from the
+//                   row statistics, and dK = scale * dS^T Q is scaled once at
+//                   the end.
 //   bwd_dq_kernel   one workgroup per (b, h, tile of 32*NW queries), built like
 //                   the forward: Q and dO rows stay in registers, K and V tiles
 //                   stream through a three-stage LDS ring; per key tile it
@@ -40,7 +41,7 @@
 #include "common.h"
 #include "kernels.h"
 
-// LDS fragments read ahead of the matrix products in bwd_kv2_kernel: row
+// LDS fragments read ahead of the matrix products in bwd_kv3_kernel: row
 // reads (S / dP) and transposed reads (dV / dK).
 #ifndef FA_KV2_PF_ROW
 #define FA_KV2_PF_ROW 2
@@ -105,26 +106,27 @@ __device__ __forceinline__ int swz(int r) {
 
 // Key-stationary dK/dV with two wave roles per 32-key block, so that two
 // waves share each SIMD and one's vector work overlaps the other's matrix
-// work.  One workgroup = 8 waves = BKV = 128 keys; wave w takes key block
-// w % 4 (waves w and w + 4 share a SIMD) and role w / 4:
-//   role 0 (S side):  S - LSE/scale = Q K^T + stat, P = exp2(. * scale * log2 e)
-//                     (causal mask), P to LDS in fp32, dV^T += dO^T P;
-//   role 1 (dP side): dP - D = dO V^T + stat, dS' = P o (dP - D) once P is
-//                     published, dK^T += Q^T dS'.
-// Each wave keeps only its side's stationary operand (K or V rows) and
-// accumulator (dV or dK): half of what one wave holding both needs.  The dK
-// products of a query tile run one tile late, in the first phase of the next
-// tile, where they fill the matrix unit while the S side computes P:
-//   phase 1: role 0 S(i), P(i) to LDS     | role 1 dP(i), dK += dS'(i-1)
-//   barrier (tile i+1 landed), copy of tile i+2 into the stage of tile i-1
-//   phase 2: role 0 dV += P(i)            | role 1 dS'(i) from P(i)
-//            both: row statistics of tile i+1 into the S / dP accumulators
-//   barrier (P(i) read)
-// Query tiles of BQ rows (Q, dO, row statistics) stream through a
-// three-stage ring.
+// work.  One workgroup = 8 waves = 128 keys; wave w takes key block w % 4
+// (waves w and w + 4 share a SIMD) and role w / 4.  Each wave keeps only its
+// side's stationary operand (K or V rows of its 32 keys) and accumulator (dV
+// or dK): half of what one wave holding both would need, so two waves fit per
+// SIMD.  One barrier per query tile, and the same matrix work in both roles:
+//   role 0 (S side):  S(i), P(i) = exp2(..) (causal mask), P(i) to LDS in the
+//                     input type, dV^T += dO(i)^T P(i)          (32 products)
+//   role 1 (dP side): dS'(i-1) = P(i-1) o (dP(i-1) - D) with P(i-1) from LDS
+//                     and dP(i-1) - D kept in registers since the previous
+//                     tile, dK^T += Q(i-1)^T dS'(i-1), then dP(i) - D
+//                                                               (32 products)
+//   barrier: P(i) published, tile i+1 landed.
+// P passes through two LDS buffers (tile parity), so the single barrier per
+// tile orders both its writes and its reads.  P is exchanged in the input
+// type (the same rounding that feeds dV^T += dO^T P), which keeps both
+// buffers inside LDS next to three query-tile stages; dS' is formed from it
+// in fp32.  Tile i+1 is copied at the start of tile i into the stage of tile
+// i-2, free since the previous barrier.
 template <int D, int BQ, bool CAUSAL, int DT>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-bwd_kv2_kernel(BwdArgs a) {
+bwd_kv3_kernel(BwdArgs a) {
   using E = Elem<DT>;
   using v8 = typename E::v8;
   constexpr int NW = 8;
@@ -135,15 +137,15 @@ bwd_kv2_kernel(BwdArgs a) {
   constexpr int STAGEB = 2 * QTB + RSB;
   constexpr int NSTG = 3;
   constexpr int NQB = BQ / 32;
-  constexpr int PLANE = 32 * 256;    // fp32 P of one key block: 32 rows of 256 bytes
+  constexpr int PBUF = 4 * 64 * NQB * 2 * 16;  // P of the four key blocks, one tile
   constexpr int CH_ROW = D / 8;
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
   static_assert(QTB % (1024 * NW) == 0, "a Q tile must split into whole 1 KiB copies per wave");
-  static_assert(BQ == 64, "P exchange rows hold 64 queries");
+  static_assert(BQ == 64, "four 16-byte P chunks per lane");
   constexpr int IPW = QTB / 1024 / NW;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTG * STAGEB + 4 * PLANE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTG * STAGEB + 2 * PBUF];
   FA_LDS uint8_t* lds = (FA_LDS uint8_t*)smem;
   FA_LDS uint8_t* p_lds = lds + NSTG * STAGEB;
 
@@ -190,29 +192,16 @@ bwd_kv2_kernel(BwdArgs a) {
       dma16_buf(r, (uint32_t)lane * 16, sb + 2 * QTB + wave * 1024);
     }
   };
-  // Copies issued per tile: 2 IPW, plus one statistics copy for waves 0, 1.
-  auto first_tile_sync = [&]() {
-    if (wave < 2)
-      dma_sync<2 * IPW + 1>();
-    else
-      dma_sync<2 * IPW>();
-  };
-  // Mid-tile: every copy issued so far (those of the next tile) has landed
-  // and this wave's LDS writes are visible to the workgroup.
-  auto mid_sync = [&]() {
+  // Every copy issued so far has landed, this wave's LDS writes are
+  // complete, then the workgroup barrier.
+  auto tile_sync = [&]() {
     wait_vmcnt<0>();
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt, expcnt untouched
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  auto end_sync = [&]() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
 
-  // LDS read offsets within a Q / dO tile (rows, and transposed reads).
   int roff[NDC];
   {
     const int f = swz<D>(l32);
@@ -240,12 +229,13 @@ bwd_kv2_kernel(BwdArgs a) {
     const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
     return __builtin_bit_cast(v8, u32x4_t{l2[0], l2[1], h2[0], h2[1]});
   };
-  // P exchange: the lanes of a key block form 32 rows of 256 bytes (row l32,
-  // 16-byte chunk 2 m + hl for chunk m = registers 4(m%4)..+3 of query block
-  // m/4), XOR-swizzled like the row reads of a Q tile.
-  FA_LDS uint8_t* prow = p_lds + kb * PLANE + l32 * 256;
-  const int pswz = swz<128>(l32);
-  auto pchunk = [&](int m) { return prow + 16 * ((2 * m + hl) ^ pswz); };
+  // P exchange: per key block, 64 lanes x 64 bytes (chunk m = the packed
+  // words pw[m/2][m%2], queries 16 m .. 16 m + 15), chunk index XOR-swizzled
+  // by (lane / 4) % 4 so that any 16 consecutive lanes hit 16 different
+  // 16-byte bank groups.
+  auto pchunk = [&](int buf, int m) {
+    return p_lds + buf * PBUF + kb * (64 * 64) + lane * 64 + 16 * (m ^ ((lane >> 2) & 3));
+  };
 
   const int nq = (N + BQ - 1) / BQ;
   const int i0 = CAUSAL ? k0 / BQ : 0;
@@ -253,8 +243,6 @@ bwd_kv2_kernel(BwdArgs a) {
 
   auto run = [&](auto role_tag) {
     constexpr int ROLE = decltype(role_tag)::value;
-    // Stationary operand: K rows (role 0) or V rows (role 1) of this lane's
-    // key as B operands (head-dim slots dc*16 + 8*hl + [0, 8)).
     v8 kvf[NDC];
     {
       const uint16_t* src = static_cast<const uint16_t*>(ROLE == 0 ? a.k : a.v) + base;
@@ -266,26 +254,43 @@ bwd_kv2_kernel(BwdArgs a) {
       }
     }
     // Completing these loads before the first copy is issued tells the
-    // compiler that no load of its own is outstanding inside the loop;
-    // otherwise it waits there for every copy in flight.
+    // compiler that no load of its own is outstanding inside the loop.
     wait_vmcnt<0>();
     f32x16_t acc[NDB];  // dV^T (role 0) or dK^T / scale (role 1)
 #pragma unroll
     for (int i = 0; i < NDB; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-    // P (role 0) or dS' of the previous tile (role 1) packed as B operands:
-    // pw[qb][h] covers queries qb*32 + 16 h + [0, 16).
-    uint32_t pw[NQB][2][4];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) pw[qb][h][t] = 0u;
+    // sacc: S - LSE/scale (role 0, this tile) or dP - D (role 1, kept one
+    // tile); register r of block qb is query row qb*32 + 8*(r/4) + 4*hl + r%4.
+    f32x16_t sacc[NQB];
+    uint32_t pw[NQB][2][4];  // P (role 0) or dS' (role 1) as B operands
 
-    // acc += T^T W over the 64 queries of a tile: T = dO (role 0) or Q
-    // (role 1) read transposed, W = pw; 16 queries per instruction.
+    auto load_stats = [&](const FA_LDS uint8_t* sb) {
+      const FA_LDS uint8_t* ps = sb + 2 * QTB + ROLE * 1024 + 16 * hl;
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4_t v = *(const FA_LDS f32x4_t*)(ps + (qb * 32 + 8 * g) * 4);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) sacc[qb][4 * g + t] = v[t];
+        }
+    };
+    // sacc += T K^T or T V^T over the tile's rows T (Q or dO).
+    auto row_products = [&](const FA_LDS uint8_t* src) {
+      constexpr int PF = FA_KV2_PF_ROW, NST = NQB * NDC;
+      v8 fr[PF + 1];
+#pragma unroll
+      for (int s = 0; s < PF; ++s) fr[s] = ld_row(src, s / NDC, s % NDC);
+#pragma unroll
+      for (int s = 0; s < NST; ++s) {
+        if (s + PF < NST) fr[(s + PF) % (PF + 1)] = ld_row(src, (s + PF) / NDC, (s + PF) % NDC);
+        sacc[s / NDC] = E::mfma(fr[s % (PF + 1)], kvf[s % NDC], sacc[s / NDC]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // acc += T^T W over the 64 queries of a tile (T read transposed, W = pw).
     auto acc_products = [&](const FA_LDS uint8_t* src) {
       constexpr int PF = FA_KV2_PF_TR, NST = NDB * (BQ / 16);
       v8 fr[PF + 1];
@@ -301,117 +306,89 @@ bwd_kv2_kernel(BwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-
-    // sacc = S - LSE/scale (role 0) or dP - D (role 1) of the current tile;
-    // register r of block qb is query row qb*32 + 8*(r/4) + 4*hl + r%4.  It
-    // starts from the row statistics, loaded one tile ahead.
-    f32x16_t sacc[NQB];
-    auto load_stats = [&](int st) {
-      const FA_LDS uint8_t* ps = lds + st * STAGEB + 2 * QTB + ROLE * 1024 + 16 * hl;
+    // Role 1: dS' of the previous tile from its P (buffer pb) and the kept
+    // dP - D, packed into pw; then dK^T += Q^T dS'.
+    auto ds_and_dk = [&](int pb, const FA_LDS uint8_t* qprev) {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4_t v = *(const FA_LDS f32x4_t*)(ps + (qb * 32 + 8 * g) * 4);
+        for (int h = 0; h < 2; ++h) {
+          const u32x4_t pp = *(const FA_LDS u32x4_t*)pchunk(pb, qb * 2 + h);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) sacc[qb][4 * g + t] = v[t];
+          for (int w = 0; w < 4; ++w) {
+            // Word w holds registers 8h + 2w, 8h + 2w + 1 of block qb.
+            const int r = 8 * h + 2 * w;
+            const uint32_t word = pp[w];
+            const float lo = to_f32<DT>((uint16_t)(word & 0xffffu));
+            const float hi = to_f32<DT>((uint16_t)(word >> 16));
+            pw[qb][h][w] = E::pack2(lo * sacc[qb][r], hi * sacc[qb][r + 1]);
+          }
         }
+      acc_products(qprev);
     };
 
-    auto iteration = [&](auto m_tag, int i, int st, int sp, int sn) {
+    auto iteration = [&](auto m_tag, auto first_tag, int i, int st) {
       constexpr bool MASKED = decltype(m_tag)::value;
+      constexpr bool FIRST = decltype(first_tag)::value;
       const FA_LDS uint8_t* sb = lds + st * STAGEB;
       const int q0 = i * BQ;
-
-      // Phase 1.
-      {
-        const FA_LDS uint8_t* src = sb + (ROLE == 0 ? 0 : QTB);
-        constexpr int PF = FA_KV2_PF_ROW, NST = NQB * NDC;
-        v8 fr[PF + 1];
-#pragma unroll
-        for (int s = 0; s < PF; ++s) fr[s] = ld_row(src, s / NDC, s % NDC);
-#pragma unroll
-        for (int s = 0; s < NST; ++s) {
-          if (s + PF < NST) fr[(s + PF) % (PF + 1)] = ld_row(src, (s + PF) / NDC, (s + PF) % NDC);
-          sacc[s / NDC] = E::mfma(fr[s % (PF + 1)], kvf[s % NDC], sacc[s / NDC]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+      issue_tile(i + 1, st == 2 ? 0 : st + 1);  // the stage of tile i-2
       if constexpr (ROLE == 0) {
+        load_stats(sb);
+        row_products(sb);  // S(i) - LSE/scale
         const float c = a.scale_log2;
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            f32x4_t p4;
+          for (int h = 0; h < 2; ++h) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              float pv = fast_exp2(sacc[qb][4 * g + t] * c);
+            for (int w = 0; w < 4; ++w) {
+              const int r = 8 * h + 2 * w;
+              float p0 = fast_exp2(sacc[qb][r] * c), p1 = fast_exp2(sacc[qb][r + 1] * c);
               if constexpr (MASKED) {
-                if (key > q0 + qb * 32 + 8 * g + 4 * hl + t) pv = 0.f;
+                const int q = q0 + qb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+                if (key > q) p0 = 0.f;
+                if (key > q + 1) p1 = 0.f;
               }
-              p4[t] = pv;
+              pw[qb][h][w] = E::pack2(p0, p1);
             }
-            *(FA_LDS f32x4_t*)pchunk(qb * 4 + g) = p4;
-            pw[qb][g >> 1][2 * (g & 1)] = E::pack2(p4[0], p4[1]);
-            pw[qb][g >> 1][2 * (g & 1) + 1] = E::pack2(p4[2], p4[3]);
+            *(FA_LDS u32x4_t*)pchunk(i & 1, qb * 2 + h) =
+                u32x4_t{pw[qb][h][0], pw[qb][h][1], pw[qb][h][2], pw[qb][h][3]};
           }
-      } else {
-        acc_products(lds + sp * STAGEB);  // dK^T += Q(i-1)^T dS'(i-1)
-      }
-      mid_sync();
-      issue_tile(i + 2, sp);  // the stage of tile i-1, now read by every wave
-
-      // Phase 2.
-      if constexpr (ROLE == 0) {
         acc_products(sb + QTB);  // dV^T += dO(i)^T P(i)
       } else {
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4_t p4 = *(const FA_LDS f32x4_t*)pchunk(qb * 4 + g);
-            float ds[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) ds[t] = p4[t] * sacc[qb][4 * g + t];
-            pw[qb][g >> 1][2 * (g & 1)] = E::pack2(ds[0], ds[1]);
-            pw[qb][g >> 1][2 * (g & 1) + 1] = E::pack2(ds[2], ds[3]);
-          }
+        if constexpr (!FIRST) ds_and_dk((i - 1) & 1, lds + (st == 0 ? 2 : st - 1) * STAGEB);
+        load_stats(sb);
+        row_products(sb + QTB);  // dP(i) - D, kept for the next tile
       }
-      load_stats(sn);  // tile i+1 landed before the mid-tile barrier
-      // Orders this tile's P reads before the next tile's P writes.
-      end_sync();
+      tile_sync();  // P(i) published; tile i+1 landed
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
 
     if (i0 < nq) {
-      // Stage 2 starts as an all-zero "tile i0-1" for the first deferred dK
-      // products (zero dS' against zero Q).
-      issue_tile(i0 - 1, 2);
       issue_tile(i0, 0);
-      issue_tile(i0 + 1, 1);
-      first_tile_sync();
-      load_stats(0);
-      int st = 0, sp = 2, i = i0;
+      tile_sync();
+      int st = 0, i = i0;
+      if (i < i_unmask)
+        iteration(T_{}, T_{}, i, st);
+      else
+        iteration(F_{}, T_{}, i, st);
+      st = 1;
+      ++i;
       for (; i < i_unmask; ++i) {
-        const int sn = st == 2 ? 0 : st + 1;
-        iteration(T_{}, i, st, sp, sn);
-        sp = st;
-        st = sn;
+        iteration(T_{}, F_{}, i, st);
+        st = st == 2 ? 0 : st + 1;
       }
       for (; i < nq; ++i) {
-        const int sn = st == 2 ? 0 : st + 1;
-        iteration(F_{}, i, st, sp, sn);
-        sp = st;
-        st = sn;
+        iteration(F_{}, F_{}, i, st);
+        st = st == 2 ? 0 : st + 1;
       }
-      if constexpr (ROLE == 1) acc_products(lds + sp * STAGEB);  // dK of the last tile
+      // Role 1: dK of the last tile (its P was published by the last barrier).
+      if constexpr (ROLE == 1) ds_and_dk((nq - 1) & 1, lds + (st == 0 ? 2 : st - 1) * STAGEB);
     }
     wait_vmcnt<0>();  // copies past the last tile must land before LDS is released
 
-    // dV (role 0) or dK = scale * dS'^T Q (role 1) for this lane's key:
-    // register r of head-dim block db is head dim db*32 + 8*(r/4) + 4*hl + r%4.
     if (key < N) {
       uint16_t* row = static_cast<uint16_t*>(ROLE == 0 ? a.dv : a.dk) + base + (int64_t)key * D;
       const float f = ROLE == 0 ? 1.0f : a.scale;
@@ -690,9 +667,9 @@ hipError_t launch_d(const BwdArgs& a0, int BH, bool causal, hipStream_t s) {
   int64_t grid = (int64_t)a.n_ktiles * BH;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (causal)
-    hipLaunchKernelGGL((bwd_kv2_kernel<D, BQ, true, DT>), dim3((unsigned)grid), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((bwd_kv3_kernel<D, BQ, true, DT>), dim3((unsigned)grid), dim3(512), 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_kv2_kernel<D, BQ, false, DT>), dim3((unsigned)grid), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((bwd_kv3_kernel<D, BQ, false, DT>), dim3((unsigned)grid), dim3(512), 0, s, a);
 
   e = hipGetLastError();
   if (e != hipSuccess) return e;
