@@ -19,7 +19,9 @@
 //     e4m3 maximum); the row normaliser is summed from the fp32 P~;
 //   * the output accumulator is kept in units of one value block's scale;
 //     when the next P V product uses another block (every 128 keys) it is
-//     multiplied by vs_old / vs_new, together with any reference raise;
+//     multiplied by vs_old / vs_new under the matrix products of the
+//     iteration before, and by the factor of a reference raise at the end of
+//     a tile;
 //   * V8 stays row-major in LDS and is read transposed with ds_read_b64_tr_b8
 //     (inside a 16-lane group, lane j's byte e is byte j%8 of the chunk
 //     addressed by lane 2e + j/8); 16-byte chunks of a V row are XOR-swizzled
@@ -214,8 +216,17 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   // ---- Probabilities of one tile (scores already multiplied to log2 units
   // by mul) against the reference -m_neg, packed as e4m3; returns the lane's
   // fp32 sum of the unrounded values.
+  // Partial sums start at -0, the additive identity, so that the first
+  // addition folds away.  The packing of four probabilities writes the low
+  // half of a word, then the high half; the word's old content is passed for
+  // the untouched half of the first write (it is overwritten by the second),
+  // which saves materialising a zero.
+  auto pack4 = [](float p0, float p1, float p2, float p3, int old) {
+    const int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, old, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
+  };
   auto phase_p = [&](const Scores& s, Probs& pw, float mul, float m_neg) {
-    float ps0 = 0.f, ps1 = 0.f;
+    float ps0 = -0.f, ps1 = -0.f;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const f32x16_t& sb = s[w >> 2];
@@ -225,10 +236,16 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
       for (int u = 0; u < 4; ++u) p[u] = fast_exp2(fmaf(sb[r0 + u], mul, m_neg));
       ps0 += p[0] + p[2];
       ps1 += p[1] + p[3];
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-      pw[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
+      pw[w] = pack4(p[0], p[1], p[2], p[3], pw[w]);
     }
     return ps0 + ps1;
+  };
+
+  // Ratio of two value-block scales, exactly 1 for equal scales, otherwise
+  // by a hardware reciprocal (within 1 ulp; far below the e4m3 rounding of P
+  // and V).
+  auto vscale_ratio = [](float from, float to) {
+    return from == to ? 1.0f : from * __builtin_amdgcn_rcpf(to);
   };
 
   // ---- End of a tile: raise the reference if the tile's probabilities left
@@ -250,12 +267,14 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
       m_run = m_new;
       l_run *= alpha;
       Probs fresh;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) fresh[w] = pw[w];
       psum = phase_p(s, fresh, mul, m_new == -INFINITY ? 0.f : -m_new);
 #pragma unroll
       for (int w = 0; w < 8; ++w) pw[w] = (int)((uint32_t)fresh[w] | ((uint32_t)pw[w] & opaque_zero));
     }
     l_run += psum;
-    const float f = alpha * (vs_acc / vs_next);
+    const float f = alpha * vscale_ratio(vs_acc, vs_next);
     if (f != 1.0f) {  // wave-uniform: alpha is 1 unless a raise happened
       asm volatile("" ::: "memory");
 #pragma unroll
@@ -285,10 +304,17 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   // load shares its wait counter with the LDS reads, so waiting for it inside
   // the steps would also wait for every fragment read in flight.
   float ks_pre = kscale(-1), vs_pre = vscale(-1);
-  auto fused = [&](auto ds_tag, auto ms_tag, auto dp_tag, auto dpv_tag, int j, int st,
+  // VB: tile j starts a value block (j even: 128-row blocks of two 64-key
+  // tiles).  Then, once P(j-1) V(j-1) has been issued, O is re-expressed in
+  // the new block's scale by multiplying it by vs_acc / vs_j during the last
+  // S(j+1) steps, where the matrix work hides the multiplies, before P(j)
+  // V(j) is added in the next iteration; the end of the tile then finds the
+  // ratio 1 and only a reference raise rescales there.
+  auto fused = [&](auto ds_tag, auto ms_tag, auto dp_tag, auto dpv_tag, auto vb_tag, int j, int st,
                    const Scores& s_cur, Scores& s_nxt, Probs& p_cur, const Probs& p_prev) {
     constexpr bool DS = decltype(ds_tag)::value, MS = decltype(ms_tag)::value;
     constexpr bool DP = decltype(dp_tag)::value, DPV = decltype(dpv_tag)::value;
+    constexpr bool VB = decltype(vb_tag)::value && DP && DPV;
     const float ks_j = ks_pre, vs_j = vs_pre;
     ks_pre = kscale(j + 1);
     vs_pre = vscale(j + 1);
@@ -297,13 +323,18 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
     const FA_LDS uint8_t* vs = lds + (NSTG + sprev(st)) * TILEB;
     const float mul = qmul * ks_j;  // tile j's scores to log2 units
     const float m_neg = -m_run;
+    float vratio = 1.0f;
+    if constexpr (VB) {
+      vratio = vscale_ratio(vs_acc, vs_j);
+      vs_acc = vs_j;
+    }
     if constexpr (DS) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s_nxt[kb][r] = 0.f;
     }
-    float ps0 = 0.f, ps1 = 0.f;
+    float ps0 = -0.f, ps1 = -0.f;
     // The P(j-1) V products come first and the S(j+1) products last, so O is
     // complete when the end of the tile may rescale it, while S(j+1) is not
     // needed before the next iteration.
@@ -347,8 +378,18 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
           for (int u = 0; u < 4; ++u) p[u] = fast_exp2(fmaf(sb[r0 + u], mul, m_neg));
           ps0 += p[0] + p[2];
           ps1 += p[1] + p[3];
-          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-          p_cur[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
+          p_cur[w] = pack4(p[0], p[1], p[2], p[3], p_cur[w]);
+        }
+      }
+      if constexpr (VB) {
+        // The last half of the steps: O blocks 2 (step - NSTEP/2) .. +1,
+        // whose products were issued at least NSTEP/2 steps earlier.
+        if (step >= NSTEP / 2) {
+          constexpr int PER = NDB / (NSTEP - NSTEP / 2);
+#pragma unroll
+          for (int i = 0; i < PER; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[(step - NSTEP / 2) * PER + i][r] *= vratio;
         }
       }
       if constexpr (DS && DP && DPV && OCC > 1) {
@@ -386,20 +427,22 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   issue(K, 0, lds, koff_dma);
   issue(K, 1, lds + TILEB, koff_dma);
   dma_sync<IPW>();
-  fused(T_{}, T_{}, F_{}, F_{}, -1, NSTG - 1, sB, sA, pB, pA);  // S(0) -> sA
-  fused(T_{}, T_{}, T_{}, F_{}, 0, 0, sA, sB, pA, pB);          // S(1) -> sB, P(0) -> pA
+  fused(T_{}, T_{}, F_{}, F_{}, F_{}, -1, NSTG - 1, sB, sA, pB, pA);  // S(0) -> sA
+  fused(T_{}, T_{}, T_{}, F_{}, F_{}, 0, 0, sA, sB, pA, pB);          // S(1) -> sB, P(0) -> pA
+  // j is odd in the first iteration of each trip and even (a value block
+  // starts) in the second.
   int j = 1, st = 1;
   for (; j + 2 < t_mask; j += 2) {
     const int stb = snext(st);
-    fused(T_{}, F_{}, T_{}, T_{}, j, st, sB, sA, pB, pA);
-    fused(T_{}, F_{}, T_{}, T_{}, j + 1, stb, sA, sB, pA, pB);
+    fused(T_{}, F_{}, T_{}, T_{}, F_{}, j, st, sB, sA, pB, pA);
+    fused(T_{}, F_{}, T_{}, T_{}, T_{}, j + 1, stb, sA, sB, pA, pB);
     st = snext(stb);
   }
   for (; j <= ntiles; j += 2) {
     const int stb = snext(st);
-    fused(T_{}, T_{}, T_{}, T_{}, j, st, sB, sA, pB, pA);
+    fused(T_{}, T_{}, T_{}, T_{}, F_{}, j, st, sB, sA, pB, pA);
     if (j + 1 > ntiles) break;
-    fused(T_{}, T_{}, T_{}, T_{}, j + 1, stb, sA, sB, pA, pB);
+    fused(T_{}, T_{}, T_{}, T_{}, T_{}, j + 1, stb, sA, sB, pA, pB);
     st = snext(stb);
   }
   wait_vmcnt<0>();
