@@ -182,16 +182,18 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
       for (int u = 0; u < 2; ++u) koff[dc][u] = l32 * ROWB + 16 * ((4 * dc + 2 * hl + u) ^ f);
   }
   // V^T (A operand of O^T): supplier lane 2e + c of each 16-lane group reads
-  // row tr_row(rd) of the tile and 8-byte unit db*4 + tr_unit.
+  // row 16 rd + tr_row of the tile and 8-byte unit db*4 + tr_unit.  The
+  // swizzle depends on row bits 1 and 3 only, so the four reads rd of one
+  // block sit 16 rows apart at one lane-dependent offset: one address per
+  // block, the rest in the instructions' immediate offsets.
   const int tr_e = (lane & 15) >> 1;
   const int tr_unit = ((lane >> 4) & 1) * 2 + (lane & 1);
-  int voff[NDB][4];
-#pragma unroll
-  for (int rd = 0; rd < 4; ++rd) {
-    const int row = 16 * rd + 8 * (tr_e >> 2) + 4 * hl + (tr_e & 3);
+  int voff[NDB];
+  {
+    const int row = 8 * (tr_e >> 2) + 4 * hl + (tr_e & 3);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
-      voff[db][rd] = row * ROWB + (((db * 4 + tr_unit) ^ v_swz<D>(row)) * 8);
+      voff[db] = row * ROWB + (((db * 4 + tr_unit) ^ v_swz<D>(row)) * 8);
   }
   auto ld_k = [&](const FA_LDS uint8_t* ks, int kb, int dc) {
     const FA_LDS uint8_t* p = ks + kb * 32 * ROWB;
@@ -201,9 +203,10 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   };
   auto ld_v = [&](const FA_LDS uint8_t* vs, int db) {
     i32x8_t vf;
+    const FA_LDS uint8_t* vb = vs + voff[db];
 #pragma unroll
     for (int rd = 0; rd < 4; ++rd) {
-      const i32x2_t v2 = ld_lds_tr8(vs + voff[db][rd]);
+      const i32x2_t v2 = ld_lds_tr8(vb + rd * 16 * ROWB);
       vf[2 * rd] = v2[0];
       vf[2 * rd + 1] = v2[1];
     }
