@@ -5,9 +5,10 @@
 // folded into Q's scales), V unrotated, one fp32 scale per 128-row block.
 //
 // Same structure as the 16-bit forward (query rows in registers, K/V tiles
-// copied from HBM into a three-stage LDS ring by buffer loads with an LDS
-// destination, three-stage fused pipeline S(j+1) | softmax(j) | PV(j-1),
-// S^T layout with one query per lane, lazy exp2 reference), with:
+// copied from HBM into an LDS ring by buffer loads with an LDS destination
+// (four stages and one barrier per two tiles, or three and one per tile),
+// three-stage fused pipeline S(j+1) | softmax(j) | PV(j-1), S^T layout with
+// one query per lane, lazy exp2 reference), with:
 //   * S^T = K8 Q8^T on v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3, fp32 acc);
 //     the product of the query block's and key block's scales, the softmax
 //     scale and log2(e) is one fp32 multiplier per tile (a key tile lies in
@@ -70,11 +71,14 @@ __device__ __forceinline__ int k_swz(int row) {
 
 // The key and value scales are separate read-only, non-aliased arguments so
 // that their per-tile reads can be scalar loads.
-template <int D, int BN, int NW, int OCC, bool CAUSAL>
+// NSTG = LDS stages per tensor: 4 runs the iterations in pairs with one
+// workgroup barrier per pair, 3 has one barrier per iteration (see below).
+template <int D, int BN, int NW, int OCC, int NSTG, bool CAUSAL>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
   constexpr int BM = 32 * NW;
-  constexpr int NSTG = 3;
+  static_assert(NSTG == 3 || NSTG == 4, "stage count");
+  constexpr bool PAIR = NSTG == 4;  // tile t in stage t % NSTG
   constexpr int ROWB = D;            // bytes per row
   constexpr int TILEB = BN * ROWB;
   constexpr int CH_ROW = D / 16;
@@ -140,12 +144,25 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
 #pragma unroll
     for (int jj = 0; jj < IPW; ++jj) dma16_buf(r, voff[jj], stage + (wave * IPW + jj) * 1024);
   };
-  // Iteration j copies K of tile j+3 and V of tile j+1.
+  // Tile t lives in stage t % NSTG; st = the stage of tile j, carried by the
+  // loops.  Iteration j reads K(j+1) and V(j-1).
   auto snext = [](int x) { return x == NSTG - 1 ? 0 : x + 1; };
   auto sprev = [](int x) { return x == 0 ? NSTG - 1 : x - 1; };
-  auto issue_iter = [&](int j, int st) {
-    issue(K, j + 3, lds + st * TILEB, koff_dma);
-    issue(V, j + 1, lds + (NSTG + snext(st)) * TILEB, voff_dma);
+  // Four stages: iterations run in pairs (j odd, j + 1) with one workgroup
+  // barrier per pair.  Iterations j and j + 1 read K(j+1), K(j+2), V(j-1) and
+  // V(j); the first copies K(j+3), K(j+4), V(j+1) and V(j+2), which the next
+  // pair reads, into the stages the previous pair read (free since its
+  // barrier); the second waits for those copies and ends with the barrier that
+  // publishes them.  Each copy has two iterations to land.
+  // Three stages: iteration j copies K(j+3) and V(j+1) into the stages of K(j)
+  // and V(j-2) and ends with a barrier after waiting for K(j+2) and V(j).
+  // (With four stages the stage of tile t >= -2 is (t + 4) & 3, computed
+  // from j directly; measured faster than carrying it.)
+  auto issue_pair = [&](int j) {
+    issue(K, j + 3, lds + ((j + 3) & 3) * TILEB, koff_dma);
+    issue(K, j + 4, lds + ((j + 4) & 3) * TILEB, koff_dma);
+    issue(V, j + 1, lds + (NSTG + ((j + 1) & 3)) * TILEB, voff_dma);
+    issue(V, j + 2, lds + (NSTG + ((j + 2) & 3)) * TILEB, voff_dma);
   };
 
   // Q8^T operand: lane holds query qrow, head-dim bytes dc*64 + 32*hl + [0, 32).
@@ -313,17 +330,26 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   // S(j+1) steps, where the matrix work hides the multiplies, before P(j)
   // V(j) is added in the next iteration; the end of the tile then finds the
   // ratio 1 and only a reference raise rescales there.
-  auto fused = [&](auto ds_tag, auto ms_tag, auto dp_tag, auto dpv_tag, auto vb_tag, int j, int st,
-                   const Scores& s_cur, Scores& s_nxt, Probs& p_cur, const Probs& p_prev) {
+  // SECOND: the second iteration of a pair (j even), else the first (j odd).
+  auto issue_iter = [&](int j, int st) {
+    issue(K, j + 3, lds + st * TILEB, koff_dma);
+    issue(V, j + 1, lds + (NSTG + snext(st)) * TILEB, voff_dma);
+  };
+  auto fused = [&](auto ds_tag, auto ms_tag, auto dp_tag, auto dpv_tag, auto vb_tag, auto second_tag,
+                   int j, int st, const Scores& s_cur, Scores& s_nxt, Probs& p_cur, const Probs& p_prev) {
     constexpr bool DS = decltype(ds_tag)::value, MS = decltype(ms_tag)::value;
     constexpr bool DP = decltype(dp_tag)::value, DPV = decltype(dpv_tag)::value;
     constexpr bool VB = decltype(vb_tag)::value && DP && DPV;
+    constexpr bool SECOND = decltype(second_tag)::value;
     const float ks_j = ks_pre, vs_j = vs_pre;
     ks_pre = kscale(j + 1);
     vs_pre = vscale(j + 1);
-    issue_iter(j, st);
-    const FA_LDS uint8_t* ks = lds + snext(st) * TILEB;
-    const FA_LDS uint8_t* vs = lds + (NSTG + sprev(st)) * TILEB;
+    if constexpr (!PAIR)
+      issue_iter(j, st);
+    else if constexpr (!SECOND)
+      issue_pair(j);
+    const FA_LDS uint8_t* ks = lds + (PAIR ? (j + 1) & 3 : snext(st)) * TILEB;
+    const FA_LDS uint8_t* vs = lds + (NSTG + (PAIR ? (j + 3) & 3 : sprev(st))) * TILEB;
     const float mul = qmul * ks_j;  // tile j's scores to log2 units
     const float m_neg = -m_run;
     float vratio = 1.0f;
@@ -412,7 +438,10 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
           if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s_nxt[kb][r] = -INFINITY;
     }
     if constexpr (DP) finish_tile(s_cur, p_cur, mul, ps0 + ps1, vs_j);
-    dma_sync<2 * IPW>();
+    if constexpr (!PAIR)
+      dma_sync<2 * IPW>();
+    else if constexpr (SECOND)
+      dma_sync<0>();
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
@@ -427,25 +456,27 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   // Prologue and iterations as in the 16-bit forward: tiles past the last one
   // (or past a wave's causal diagonal) come out fully masked, so their
   // probabilities and P V products are exactly zero.
+  // The prologue pair (-1, 0) reads K(0) and K(1), copied and published
+  // first.
   issue(K, 0, lds, koff_dma);
   issue(K, 1, lds + TILEB, koff_dma);
-  dma_sync<IPW>();
-  fused(T_{}, T_{}, F_{}, F_{}, F_{}, -1, NSTG - 1, sB, sA, pB, pA);  // S(0) -> sA
-  fused(T_{}, T_{}, T_{}, F_{}, F_{}, 0, 0, sA, sB, pA, pB);          // S(1) -> sB, P(0) -> pA
+  dma_sync<PAIR ? 0 : IPW>();
+  fused(T_{}, T_{}, F_{}, F_{}, F_{}, F_{}, -1, NSTG - 1, sB, sA, pB, pA);  // S(0) -> sA
+  fused(T_{}, T_{}, T_{}, F_{}, F_{}, T_{}, 0, 0, sA, sB, pA, pB);  // S(1) -> sB, P(0) -> pA
   // j is odd in the first iteration of each trip and even (a value block
   // starts) in the second.
   int j = 1, st = 1;
   for (; j + 2 < t_mask; j += 2) {
     const int stb = snext(st);
-    fused(T_{}, F_{}, T_{}, T_{}, F_{}, j, st, sB, sA, pB, pA);
-    fused(T_{}, F_{}, T_{}, T_{}, T_{}, j + 1, stb, sA, sB, pA, pB);
+    fused(T_{}, F_{}, T_{}, T_{}, F_{}, F_{}, j, st, sB, sA, pB, pA);
+    fused(T_{}, F_{}, T_{}, T_{}, T_{}, T_{}, j + 1, stb, sA, sB, pA, pB);
     st = snext(stb);
   }
   for (; j <= ntiles; j += 2) {
     const int stb = snext(st);
-    fused(T_{}, T_{}, T_{}, T_{}, F_{}, j, st, sB, sA, pB, pA);
+    fused(T_{}, T_{}, T_{}, T_{}, F_{}, F_{}, j, st, sB, sA, pB, pA);
     if (j + 1 > ntiles) break;
-    fused(T_{}, T_{}, T_{}, T_{}, T_{}, j + 1, stb, sA, sB, pA, pB);
+    fused(T_{}, T_{}, T_{}, T_{}, T_{}, T_{}, j + 1, stb, sA, sB, pA, pB);
     st = snext(stb);
   }
   wait_vmcnt<0>();
@@ -469,21 +500,22 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   }
 }
 
-template <int D, int NW, int OCC, bool CAUSAL>
+template <int D, int NW, int OCC, int NSTG, bool CAUSAL>
 hipError_t launch_one(const Fp8Args& a0, int BH, hipStream_t s) {
   constexpr int BM = 32 * NW;
   Fp8Args a = a0;
   a.n_qtiles = (a.N + BM - 1) / BM;
   const int64_t grid = (int64_t)a.n_qtiles * BH;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_fp8_kernel<D, 64, NW, OCC, CAUSAL>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, 64, NW, OCC, NSTG, CAUSAL>), dim3((unsigned)grid),
                      dim3(NW * 64), 0, s, a, a.k_scale, a.v_scale);
   return hipGetLastError();
 }
 
-template <int D, int NW, int OCC>
+template <int D, int NW, int OCC, int NSTG>
 hipError_t launch_d(const Fp8Args& a, int BH, bool causal, hipStream_t s) {
-  return causal ? launch_one<D, NW, OCC, true>(a, BH, s) : launch_one<D, NW, OCC, false>(a, BH, s);
+  return causal ? launch_one<D, NW, OCC, NSTG, true>(a, BH, s)
+                : launch_one<D, NW, OCC, NSTG, false>(a, BH, s);
 }
 
 }  // namespace
@@ -491,9 +523,12 @@ hipError_t launch_d(const Fp8Args& a, int BH, bool causal, hipStream_t s) {
 hipError_t launch_fwd_fp8(const Fp8Args& a, int B, int H, int d, bool causal, hipStream_t stream) {
   const int BH = B * H;
   switch (d) {
-    case 64: return launch_d<64, 4, 2>(a, BH, causal, stream);
-    case 128: return launch_d<128, 8, 2>(a, BH, causal, stream);
-    case 256: return launch_d<256, 4, 1>(a, BH, causal, stream);
+    // Barrier per pair of tiles where two waves share a SIMD (measured +3%
+    // at d = 64 and 128); d = 256 has one wave per SIMD and 3% more from the
+    // barrier per tile.
+    case 64: return launch_d<64, 4, 2, 4>(a, BH, causal, stream);
+    case 128: return launch_d<128, 8, 2, 4>(a, BH, causal, stream);
+    case 256: return launch_d<256, 4, 1, 3>(a, BH, causal, stream);
     default: return hipErrorInvalidValue;
   }
 }
