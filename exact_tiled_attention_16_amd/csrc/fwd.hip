@@ -11,11 +11,12 @@
 //
 // Data movement: key and value tiles of BN rows are copied from HBM straight
 // into LDS by buffer loads with an LDS destination (no staging registers),
-// into rings of three stages per tensor, two iterations ahead of their use;
-// the producers are the computing waves themselves (the pages' asynchronous
-// copies overlapped with compute, FlashAttention-3 abstract).  At the end of
-// each iteration a wave waits only for the copies the next iteration needs,
-// then the workgroup barrier publishes them.  LDS rows are unpadded; the
+// into rings of two to four stages per tensor, two iterations ahead of their
+// use; the producers are the computing waves themselves (the pages'
+// asynchronous copies overlapped with compute, FlashAttention-3 abstract).
+// At the end of each iteration (of each pair of iterations, with four stages)
+// a wave waits only for the copies the next one needs, then the workgroup
+// barrier publishes them.  LDS rows are unpadded; the
 // 16-byte chunk index of row r is XOR-ed with swz<D>(r), which keeps both LDS
 // read patterns below free of bank conflicts.
 //
@@ -122,7 +123,8 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
   static_assert(TILEB % (1024 * NW) == 0, "a tile must split into whole 1 KiB copies per wave");
   constexpr int IPW = TILEB / 1024 / NW;  // copies per wave per tensor per tile
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
-  static_assert(NSTG == 2 || NSTG == 3, "stage count");
+  static_assert(NSTG >= 2 && NSTG <= 4, "stage count");
+  constexpr bool PAIR = NSTG == 4;  // iterations in pairs, one barrier per pair
   constexpr int NKB = BN / 32;
   constexpr int NDB = D / 32;
   constexpr int NDC = D / 16;
@@ -210,6 +212,19 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
     // (j + KAHEAD) % NSTG == st; (j + VAHEAD) % NSTG == st + 1 or st.
     issue(K, j + KAHEAD, lds + st * TILEB);
     issue(V, j + VAHEAD, lds + (NSTG + (NSTG == 3 ? snext(st) : st)) * TILEB);
+  };
+  // Four stages (tile t in stage t & 3): iterations run in pairs (j odd,
+  // j + 1) with one workgroup barrier per pair.  The pair reads K(j+1),
+  // K(j+2), V(j-1) and V(j); its first iteration copies K(j+3), K(j+4),
+  // V(j+1) and V(j+2), which the next pair reads, into the stages the
+  // previous pair read (free since its barrier); the second iteration waits
+  // for those copies and ends with the barrier that publishes them.  Each
+  // copy still has two iterations to land.
+  auto issue_pair = [&](int j) {
+    issue(K, j + 3, lds + ((j + 3) & 3) * TILEB);
+    issue(K, j + 4, lds + ((j + 4) & 3) * TILEB);
+    issue(V, j + 1, lds + (NSTG + ((j + 1) & 3)) * TILEB);
+    issue(V, j + 2, lds + (NSTG + ((j + 2) & 3)) * TILEB);
   };
 
   // Q^T operand of block qb: lane holds query qw0 + 32 qb + l32, head-dim
@@ -387,13 +402,18 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
   constexpr int NSTEP = NKB * NDC;  // == (BN / 16) * NDB
   constexpr int NPAIR = NKB * 8;    // probability pairs per lane, tile and block
   constexpr int PF = D >= 256 ? 1 : 2;  // fragment prefetch distance in steps
-  auto fused = [&](auto ds_tag, auto ms_tag, auto dp_tag, auto dpv_tag, int j, int st,
-                   const Scores& s_cur, Scores& s_nxt, Probs& p_cur, const Probs& p_prev) {
+  // SECOND: the second iteration of a pair (j even), else the first.
+  auto fused = [&](auto ds_tag, auto ms_tag, auto dp_tag, auto dpv_tag, auto second_tag, int j,
+                   int st, const Scores& s_cur, Scores& s_nxt, Probs& p_cur, const Probs& p_prev) {
     constexpr bool DS = decltype(ds_tag)::value, MS = decltype(ms_tag)::value;
     constexpr bool DP = decltype(dp_tag)::value, DPV = decltype(dpv_tag)::value;
-    issue_iter(j, st);
-    const FA_LDS uint8_t* ks = lds + snext(st) * TILEB;
-    const FA_LDS uint8_t* vs = lds + (NSTG + sprev(st)) * TILEB;
+    constexpr bool SECOND = decltype(second_tag)::value;
+    if constexpr (!PAIR)
+      issue_iter(j, st);
+    else if constexpr (!SECOND)
+      issue_pair(j);
+    const FA_LDS uint8_t* ks = lds + (PAIR ? (j + 1) & 3 : snext(st)) * TILEB;
+    const FA_LDS uint8_t* vs = lds + (NSTG + (PAIR ? (j + 3) & 3 : sprev(st))) * TILEB;
     v8 kfr[PF + 1], vfr[PF + 1];
     // S(j+1) runs key block by key block (kb-major) and P(j) consumes S(j)
     // in the same order, so only about half of each score set is live at once.
@@ -476,7 +496,10 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
       for (int qb = 0; qb < QB; ++qb) psum[qb] = ps0[qb] + ps1[qb];
       finish_tile(s_cur, p_cur, psum);
     }
-    dma_sync<PENDING>();
+    if constexpr (!PAIR)
+      dma_sync<PENDING>();
+    else if constexpr (SECOND)
+      dma_sync<0>();
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
@@ -489,29 +512,32 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
   // Prologue: K(0) and K(1) in flight, wait for K(0); iteration -1 computes
   // S(0) only and issues K(2) and V(0) like any iteration; its closing wait
   // leaves exactly those in flight, so K(1) has landed for iteration 0.
+  // Four stages: the prologue pair (-1, 0) reads K(0) and K(1), copied and
+  // published first.
   issue(K, 0, lds);
-  if constexpr (NSTG == 3) {
+  if constexpr (NSTG >= 3) {
     issue(K, 1, lds + TILEB);
-    dma_sync<IPW>();
+    dma_sync<PAIR ? 0 : IPW>();
   } else {
     dma_sync<0>();
   }
-  fused(T_{}, T_{}, F_{}, F_{}, -1, NSTG - 1, sB, sA, pB, pA);  // S(0) -> sA
-  fused(T_{}, T_{}, T_{}, F_{}, 0, 0, sA, sB, pA, pB);          // S(1) -> sB, P(0) -> pA
+  fused(T_{}, T_{}, F_{}, F_{}, F_{}, -1, NSTG - 1, sB, sA, pB, pA);  // S(0) -> sA
+  fused(T_{}, T_{}, T_{}, F_{}, T_{}, 0, 0, sA, sB, pA, pB);          // S(1) -> sB, P(0) -> pA
   // Unmasked iterations two per trip, so that the score and probability
   // register sets swap roles instead of being copied; then the masked rest.
+  // j is odd in the first iteration of a trip.
   int j = 1, st = 1 % NSTG;
   for (; j + 2 < t_mask; j += 2) {
     const int stb = snext(st);
-    fused(T_{}, F_{}, T_{}, T_{}, j, st, sB, sA, pB, pA);
-    fused(T_{}, F_{}, T_{}, T_{}, j + 1, stb, sA, sB, pA, pB);
+    fused(T_{}, F_{}, T_{}, T_{}, F_{}, j, st, sB, sA, pB, pA);
+    fused(T_{}, F_{}, T_{}, T_{}, T_{}, j + 1, stb, sA, sB, pA, pB);
     st = snext(stb);
   }
   for (; j <= ntiles; j += 2) {
     const int stb = snext(st);
-    fused(T_{}, T_{}, T_{}, T_{}, j, st, sB, sA, pB, pA);
+    fused(T_{}, T_{}, T_{}, T_{}, F_{}, j, st, sB, sA, pB, pA);
     if (j + 1 > ntiles) break;
-    fused(T_{}, T_{}, T_{}, T_{}, j + 1, stb, sA, sB, pA, pB);
+    fused(T_{}, T_{}, T_{}, T_{}, T_{}, j + 1, stb, sA, sB, pA, pB);
     st = snext(stb);
   }
   wait_vmcnt<0>();  // copies past the last tile must land before LDS is released
@@ -583,7 +609,10 @@ template <int D> struct FwdCfg;
 #ifndef FA_FWD128_CFG
 #define FA_FWD128_CFG 0
 #endif
-template <> struct FwdCfg<64> { static constexpr int BN = 64, NW = 8, QB = 1, OCC = 2, NSTG = 3; };
+// d = 64 runs its iterations in pairs with one barrier per pair (four
+// stages, 64 KiB of LDS): 1.3 % faster than a barrier per tile; at d = 128
+// (128 KiB) that was 1 % slower than three stages.
+template <> struct FwdCfg<64> { static constexpr int BN = 64, NW = 8, QB = 1, OCC = 2, NSTG = 4; };
 #if FA_FWD128_CFG == 1
 template <> struct FwdCfg<128> { static constexpr int BN = 64, NW = 4, QB = 1, OCC = 2, NSTG = 2; };
 #elif FA_FWD128_CFG == 2
