@@ -6,7 +6,7 @@
 //
 // Same structure as the 16-bit forward (query rows in registers, K/V tiles
 // copied from HBM into an LDS ring by buffer loads with an LDS destination
-// (four stages and one barrier per two tiles, or three and one per tile),
+// (eight stages and one barrier per four tiles, or three and one per tile),
 // three-stage fused pipeline S(j+1) | softmax(j) | PV(j-1), S^T layout with
 // one query per lane, lazy exp2 reference), with:
 //   * S^T = K8 Q8^T on v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3, fp32 acc);
@@ -71,14 +71,17 @@ __device__ __forceinline__ int k_swz(int row) {
 
 // The key and value scales are separate read-only, non-aliased arguments so
 // that their per-tile reads can be scalar loads.
-// NSTG = LDS stages per tensor: 4 runs the iterations in pairs with one
-// workgroup barrier per pair, 3 has one barrier per iteration (see below).
+// NSTG = LDS stages per tensor: 8 runs the iterations in groups of four with
+// one workgroup barrier per group, 3 has one barrier per iteration (see
+// below).
 template <int D, int BN, int NW, int OCC, int NSTG, bool CAUSAL>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
   constexpr int BM = 32 * NW;
-  static_assert(NSTG == 3 || NSTG == 4, "stage count");
-  constexpr bool PAIR = NSTG == 4;  // tile t in stage t % NSTG
+  static_assert(NSTG == 3 || NSTG == 8, "stage count");
+  constexpr bool GROUPED = NSTG == 8;  // tile t in stage t % NSTG; groups of G iterations
+  constexpr int G = NSTG / 2;       // iterations per barrier
+  constexpr int MSK = NSTG - 1;
   constexpr int ROWB = D;            // bytes per row
   constexpr int TILEB = BN * ROWB;
   constexpr int CH_ROW = D / 16;
@@ -148,21 +151,24 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   // loops.  Iteration j reads K(j+1) and V(j-1).
   auto snext = [](int x) { return x == NSTG - 1 ? 0 : x + 1; };
   auto sprev = [](int x) { return x == 0 ? NSTG - 1 : x - 1; };
-  // Four stages: iterations run in pairs (j odd, j + 1) with one workgroup
-  // barrier per pair.  Iterations j and j + 1 read K(j+1), K(j+2), V(j-1) and
-  // V(j); the first copies K(j+3), K(j+4), V(j+1) and V(j+2), which the next
-  // pair reads, into the stages the previous pair read (free since its
-  // barrier); the second waits for those copies and ends with the barrier that
-  // publishes them.  Each copy has two iterations to land.
+  // Eight stages: iterations run in groups of G = 4 (j odd .. j + 3) with one
+  // workgroup barrier per group.  A group reads K(j+1 .. j+G) and
+  // V(j-1 .. j+G-2); its first iteration copies K(j+G+1 .. j+2G) and
+  // V(j+G-1 .. j+2G-2), which the next group reads, into the stages the
+  // previous group read (free since its barrier); its last iteration waits
+  // for those copies and ends with the barrier that publishes them.  The
+  // prologue pair (-1, 0) reads K(0) and K(1) and copies K(2 .. G+1) and
+  // V(0 .. G-1).  The stage of tile t >= -2 is computed from t directly
+  // (measured faster than carrying it).  Fewer barriers shorten the time the
+  // leading wave of a SIMD waits for the other: one barrier per two tiles was
+  // 3-4 % faster than one per tile, one per four another 2-4 %.
   // Three stages: iteration j copies K(j+3) and V(j+1) into the stages of K(j)
   // and V(j-2) and ends with a barrier after waiting for K(j+2) and V(j).
-  // (With four stages the stage of tile t >= -2 is (t + 4) & 3, computed
-  // from j directly; measured faster than carrying it.)
-  auto issue_pair = [&](int j) {
-    issue(K, j + 3, lds + ((j + 3) & 3) * TILEB, koff_dma);
-    issue(K, j + 4, lds + ((j + 4) & 3) * TILEB, koff_dma);
-    issue(V, j + 1, lds + (NSTG + ((j + 1) & 3)) * TILEB, voff_dma);
-    issue(V, j + 2, lds + (NSTG + ((j + 2) & 3)) * TILEB, voff_dma);
+  auto issue_range = [&](int k0, int v0) {
+#pragma unroll
+    for (int i = 0; i < G; ++i) issue(K, k0 + i, lds + ((k0 + i) & MSK) * TILEB, koff_dma);
+#pragma unroll
+    for (int i = 0; i < G; ++i) issue(V, v0 + i, lds + (NSTG + ((v0 + i) & MSK)) * TILEB, voff_dma);
   };
 
   // Q8^T operand: lane holds query qrow, head-dim bytes dc*64 + 32*hl + [0, 32).
@@ -330,26 +336,29 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   // S(j+1) steps, where the matrix work hides the multiplies, before P(j)
   // V(j) is added in the next iteration; the end of the tile then finds the
   // ratio 1 and only a reference raise rescales there.
-  // SECOND: the second iteration of a pair (j even), else the first (j odd).
   auto issue_iter = [&](int j, int st) {
     issue(K, j + 3, lds + st * TILEB, koff_dma);
     issue(V, j + 1, lds + (NSTG + snext(st)) * TILEB, voff_dma);
   };
-  auto fused = [&](auto ds_tag, auto ms_tag, auto dp_tag, auto dpv_tag, auto vb_tag, auto second_tag,
+  auto fused = [&](auto ds_tag, auto ms_tag, auto dp_tag, auto dpv_tag, auto vb_tag, auto pos_tag,
                    int j, int st, const Scores& s_cur, Scores& s_nxt, Probs& p_cur, const Probs& p_prev) {
     constexpr bool DS = decltype(ds_tag)::value, MS = decltype(ms_tag)::value;
     constexpr bool DP = decltype(dp_tag)::value, DPV = decltype(dpv_tag)::value;
     constexpr bool VB = decltype(vb_tag)::value && DP && DPV;
-    constexpr bool SECOND = decltype(second_tag)::value;
+    // POS: -2 / -1 = first / second iteration of the prologue, else the
+    // position in a group (0 .. G-1; 0 and 1 with three stages).
+    constexpr int POS = decltype(pos_tag)::value;
     const float ks_j = ks_pre, vs_j = vs_pre;
     ks_pre = kscale(j + 1);
     vs_pre = vscale(j + 1);
-    if constexpr (!PAIR)
+    if constexpr (!GROUPED)
       issue_iter(j, st);
-    else if constexpr (!SECOND)
-      issue_pair(j);
-    const FA_LDS uint8_t* ks = lds + (PAIR ? (j + 1) & 3 : snext(st)) * TILEB;
-    const FA_LDS uint8_t* vs = lds + (NSTG + (PAIR ? (j + 3) & 3 : sprev(st))) * TILEB;
+    else if constexpr (POS == -2)
+      issue_range(2, 0);
+    else if constexpr (POS == 0)
+      issue_range(j + G + 1, j + G - 1);
+    const FA_LDS uint8_t* ks = lds + (GROUPED ? (j + 1) & MSK : snext(st)) * TILEB;
+    const FA_LDS uint8_t* vs = lds + (NSTG + (GROUPED ? (j - 1) & MSK : sprev(st))) * TILEB;
     const float mul = qmul * ks_j;  // tile j's scores to log2 units
     const float m_neg = -m_run;
     float vratio = 1.0f;
@@ -438,9 +447,9 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
           if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s_nxt[kb][r] = -INFINITY;
     }
     if constexpr (DP) finish_tile(s_cur, p_cur, mul, ps0 + ps1, vs_j);
-    if constexpr (!PAIR)
+    if constexpr (!GROUPED)
       dma_sync<2 * IPW>();
-    else if constexpr (SECOND)
+    else if constexpr (POS == -1 || POS == G - 1)
       dma_sync<0>();
   };
   using T_ = std::true_type;
@@ -460,24 +469,47 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   // first.
   issue(K, 0, lds, koff_dma);
   issue(K, 1, lds + TILEB, koff_dma);
-  dma_sync<PAIR ? 0 : IPW>();
-  fused(T_{}, T_{}, F_{}, F_{}, F_{}, F_{}, -1, NSTG - 1, sB, sA, pB, pA);  // S(0) -> sA
-  fused(T_{}, T_{}, T_{}, F_{}, F_{}, T_{}, 0, 0, sA, sB, pA, pB);  // S(1) -> sB, P(0) -> pA
-  // j is odd in the first iteration of each trip and even (a value block
-  // starts) in the second.
+  dma_sync<GROUPED ? 0 : IPW>();
+  using PM2 = std::integral_constant<int, -2>;
+  using PM1 = std::integral_constant<int, -1>;
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  using P3 = std::integral_constant<int, 3>;
+  fused(T_{}, T_{}, F_{}, F_{}, F_{}, PM2{}, -1, NSTG - 1, sB, sA, pB, pA);  // S(0) -> sA
+  fused(T_{}, T_{}, T_{}, F_{}, F_{}, PM1{}, 0, 0, sA, sB, pA, pB);  // S(1) -> sB, P(0) -> pA
   int j = 1, st = 1;
-  for (; j + 2 < t_mask; j += 2) {
-    const int stb = snext(st);
-    fused(T_{}, F_{}, T_{}, T_{}, F_{}, F_{}, j, st, sB, sA, pB, pA);
-    fused(T_{}, F_{}, T_{}, T_{}, T_{}, T_{}, j + 1, stb, sA, sB, pA, pB);
-    st = snext(stb);
-  }
-  for (; j <= ntiles; j += 2) {
-    const int stb = snext(st);
-    fused(T_{}, T_{}, T_{}, T_{}, F_{}, F_{}, j, st, sB, sA, pB, pA);
-    if (j + 1 > ntiles) break;
-    fused(T_{}, T_{}, T_{}, T_{}, T_{}, T_{}, j + 1, stb, sA, sB, pA, pB);
-    st = snext(stb);
+  // j is odd at the start of a trip; even iterations start a value block.
+  if constexpr (NSTG == 3) {
+    for (; j + 2 < t_mask; j += 2) {
+      const int stb = snext(st);
+      fused(T_{}, F_{}, T_{}, T_{}, F_{}, P0{}, j, st, sB, sA, pB, pA);
+      fused(T_{}, F_{}, T_{}, T_{}, T_{}, P1{}, j + 1, stb, sA, sB, pA, pB);
+      st = snext(stb);
+    }
+    for (; j <= ntiles; j += 2) {
+      const int stb = snext(st);
+      fused(T_{}, T_{}, T_{}, T_{}, F_{}, P0{}, j, st, sB, sA, pB, pA);
+      if (j + 1 > ntiles) break;
+      fused(T_{}, T_{}, T_{}, T_{}, T_{}, P1{}, j + 1, stb, sA, sB, pA, pB);
+      st = snext(stb);
+    }
+  } else {
+    for (; j + 4 < t_mask; j += 4) {
+      fused(T_{}, F_{}, T_{}, T_{}, F_{}, P0{}, j, 0, sB, sA, pB, pA);
+      fused(T_{}, F_{}, T_{}, T_{}, T_{}, P1{}, j + 1, 0, sA, sB, pA, pB);
+      fused(T_{}, F_{}, T_{}, T_{}, F_{}, P2{}, j + 2, 0, sB, sA, pB, pA);
+      fused(T_{}, F_{}, T_{}, T_{}, T_{}, P3{}, j + 3, 0, sA, sB, pA, pB);
+    }
+    for (; j <= ntiles; j += 4) {
+      fused(T_{}, T_{}, T_{}, T_{}, F_{}, P0{}, j, 0, sB, sA, pB, pA);
+      if (j + 1 > ntiles) break;
+      fused(T_{}, T_{}, T_{}, T_{}, T_{}, P1{}, j + 1, 0, sA, sB, pA, pB);
+      if (j + 2 > ntiles) break;
+      fused(T_{}, T_{}, T_{}, T_{}, F_{}, P2{}, j + 2, 0, sB, sA, pB, pA);
+      if (j + 3 > ntiles) break;
+      fused(T_{}, T_{}, T_{}, T_{}, T_{}, P3{}, j + 3, 0, sA, sB, pA, pB);
+    }
   }
   wait_vmcnt<0>();
 
@@ -523,11 +555,11 @@ hipError_t launch_d(const Fp8Args& a, int BH, bool causal, hipStream_t s) {
 hipError_t launch_fwd_fp8(const Fp8Args& a, int B, int H, int d, bool causal, hipStream_t stream) {
   const int BH = B * H;
   switch (d) {
-    // Barrier per pair of tiles where two waves share a SIMD (measured +3%
-    // at d = 64 and 128); d = 256 has one wave per SIMD and 3% more from the
-    // barrier per tile.
-    case 64: return launch_d<64, 4, 2, 4>(a, BH, causal, stream);
-    case 128: return launch_d<128, 8, 2, 4>(a, BH, causal, stream);
+    // One barrier per four tiles where two waves share a SIMD (d = 64, 128);
+    // d = 256 has one wave per SIMD and measured 3 % faster with a barrier
+    // per tile than with one per pair.
+    case 64: return launch_d<64, 4, 2, 8>(a, BH, causal, stream);
+    case 128: return launch_d<128, 8, 2, 8>(a, BH, causal, stream);
     case 256: return launch_d<256, 4, 1, 3>(a, BH, causal, stream);
     default: return hipErrorInvalidValue;
   }
