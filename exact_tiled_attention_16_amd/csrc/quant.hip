@@ -13,6 +13,8 @@
 // A block is FA_FP8_BLOCK = 128 rows of one (b, h), all d columns.  Each row is
 // held by d/8 consecutive lanes, 8 elements per lane; butterflies of
 // half-width < 8 stay inside a lane, wider ones pair lane t with lane t ^ (h/8).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -29,6 +31,24 @@ template <> __device__ __forceinline__ float elem_to_f32<0>(uint32_t b) {
 }
 template <> __device__ __forceinline__ float elem_to_f32<1>(uint32_t b) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+// Value of the lane `hl` away inside a 16-lane row (hl = 1, 2, 4, 8) by data
+// parallel primitives (no LDS traffic): quad permutations for 1 and 2, row
+// shifts for 4 and 8 (a lane whose bit hl is clear reads lane + hl, one whose
+// bit is set reads lane - hl).
+template <int HL>
+__device__ __forceinline__ float lane_xor_in_row(float v, bool upper) {
+  const int b = __builtin_bit_cast(int, v);
+  if constexpr (HL == 1) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false));
+  } else if constexpr (HL == 2) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, false));
+  } else {
+    const int from_above = __builtin_amdgcn_update_dpp(0, b, 0x100 + HL, 0xF, 0xF, false);
+    const int from_below = __builtin_amdgcn_update_dpp(0, b, 0x110 + HL, 0xF, 0xF, false);
+    return __builtin_bit_cast(float, upper ? from_below : from_above);
+  }
 }
 
 // MODE 0: block scales, quantise.  MODE 1: write the block amax only.
@@ -80,18 +100,29 @@ quant_kernel(QuantArgs a) {
           }
         }
       }
-      // Half-widths 8 .. D/2: partner lane t ^ (h/8) within the row's lanes.
+      // Half-widths 8 .. D/2: partner lane t ^ (h/8) within the row's lanes
+      // (inside a 16-lane row by data-parallel moves, across rows by a lane
+      // shuffle).
       const int t = c % TPR;
-#pragma unroll
-      for (int hl = 1; hl < TPR; hl <<= 1) {
-        const bool upper = (t & hl) != 0;
+      auto level = [&](auto hl_tag) {
+        constexpr int HL = decltype(hl_tag)::value;
+        const bool upper = (t & HL) != 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float mine = x[i][e];
-          const float other = __shfl_xor(mine, hl, TPR);
+          float other;
+          if constexpr (HL < 16)
+            other = lane_xor_in_row<HL>(mine, upper);
+          else
+            other = __shfl_xor(mine, HL, TPR);
           x[i][e] = upper ? (other - mine) : (mine + other);
         }
-      }
+      };
+      if constexpr (TPR > 1) level(std::integral_constant<int, 1>{});
+      if constexpr (TPR > 2) level(std::integral_constant<int, 2>{});
+      if constexpr (TPR > 4) level(std::integral_constant<int, 4>{});
+      if constexpr (TPR > 8) level(std::integral_constant<int, 8>{});
+      if constexpr (TPR > 16) level(std::integral_constant<int, 16>{});
     }
     if (row < N) {
 #pragma unroll
@@ -119,6 +150,16 @@ quant_kernel(QuantArgs a) {
   }
 
   const float scale = block_amax > 0.f ? block_amax / 448.0f : 1.0f;
+  // x / scale correctly rounded (IEEE division) from the correctly rounded
+  // reciprocal and one residual step: for q0 within 1 ulp of x / scale and
+  // rinv within half an ulp of 1 / scale, q0 + fma(-q0, scale, x) * rinv is
+  // the correctly rounded quotient (Markstein, IBM J. Res. Dev. 34(1), 1990)
+  // outside the subnormal range, where every code is zero anyway.
+  const float rinv = 1.0f / scale;
+  auto quotient = [&](float v) {
+    const float q0 = v * rinv;
+    return fmaf(fmaf(-q0, scale, v), rinv, q0);
+  };
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int c = tid + i * kThreads;
@@ -132,7 +173,7 @@ quant_kernel(QuantArgs a) {
       float y[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        y[e] = fminf(fmaxf(x[i][4 * j + e] / scale, -448.0f), 448.0f);
+        y[e] = fminf(fmaxf(quotient(x[i][4 * j + e]), -448.0f), 448.0f);
       int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
       w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
       out[j] = (uint32_t)w;
