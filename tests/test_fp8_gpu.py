@@ -106,8 +106,11 @@ def _dev_fwd_fp8(ops, causal):
     return o.to(torch.float64).cpu().numpy(), lse.to(torch.float64).cpu().numpy()
 
 
+# 1 .. 9 key tiles of 64: the kernel takes tiles in groups of four with one
+# barrier per group, and these lengths end the last group after each of its
+# positions (and ragged or whole).
 @pytest.mark.parametrize("d", [64, 128, 256])
-@pytest.mark.parametrize("N", [1, 65, 200, 513])
+@pytest.mark.parametrize("N", [1, 65, 150, 200, 448, 513])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fwd_fp8_against_dequantised_oracle(d, N, causal):
     _banner(f"fwd_fp8 d={d} N={N} causal={causal}")
