@@ -31,7 +31,9 @@ step's attention flop divided by its wall time (HIP events on the launch
 stream around exactly --steps steps); per-leg figures and the roofline of the
 dominant kernel (average launch duration from per-launch events) are printed
 in the same JSON line, next to the fp64 oracle timed on a bounded sample on
-the host cores.
+the host cores.  The oracle leg also scores the FP8 path (block scales and
+rotation) against per-tensor-scaled FP8 on the FP8 workload's outlier-injected
+inputs (cpu_baseline.fp8_accuracy: RMSE of four heads against the oracle).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                       [--no-next-rows]
@@ -448,6 +450,48 @@ def cpu_baseline(legs_present, budget_s=15.0, gpu_out=None):
                       f"{dt:.1f} s wall"}
 
 
+def fp8_accuracy(fa, torch, dev):
+    """Error of the FP8 path with block scales and the Hadamard rotation
+    against per-tensor-scaled FP8 without rotation (the same kernel), on the
+    FP8 workload's outlier-injected inputs (B=4, H=16, N=4096, d=128, 0.1 %
+    of entries ~ N(0, 10^2)): RMSE over four whole heads against the fp64
+    oracle on the bf16 values both quantised.  Part of the oracle leg."""
+    import numpy as np
+    from exact_tiled_attention_16_amd import inputs
+    from oracle import attention as oatt
+    B, H, N, d, wid = 4, 16, 4096, 128, 4
+    host = [torch.from_numpy(x).to(torch.bfloat16) for x in inputs.qkv_outliers(B, H, N, d, wid)]
+    qd, kd, vd = (t.to(dev) for t in host)
+    sg = torch.from_numpy(inputs.signs(d, wid)).to(dev)
+
+    def run(rotate, per_tensor):
+        s = sg if rotate else None
+        q8, qs = fa.quant_fp8(qd, signs=s, scale_mul=1.0 / d if rotate else 1.0,
+                              per_tensor=per_tensor)
+        k8, ks = fa.quant_fp8(kd, signs=s, per_tensor=per_tensor)
+        v8, vs = fa.quant_fp8(vd, per_tensor=per_tensor)
+        o, _ = fa.fwd_fp8(q8, k8, v8, qs, ks, vs)
+        return o
+    outs = {"block_rotated": run(True, False), "per_tensor": run(False, True),
+            "bf16_path": fa.fwd(qd, kd, vd)[0]}
+    torch.cuda.synchronize()
+    heads = [(0, 0), (1, 5), (2, 10), (3, 15)]
+    sq = {name: 0.0 for name in outs}
+    for b, h in heads:
+        q64, k64, v64 = (t[b:b + 1, h:h + 1].to(torch.float64).numpy() for t in host)
+        ref, _ = oatt.attention_fwd(q64, k64, v64)
+        for name, o in outs.items():
+            sq[name] += float(np.mean((o[b, h].to(torch.float64).cpu().numpy() - ref[0, 0]) ** 2))
+    r = {name: (v / len(heads)) ** 0.5 for name, v in sq.items()}
+    return {"workload": f"B={B} H={H} N={N} d={d}, Q/K/V N(0,1) with 0.1% outliers of std 10",
+            "heads": len(heads),
+            "rmse_block_rotated": float(f"{r['block_rotated']:.4e}"),
+            "rmse_per_tensor": float(f"{r['per_tensor']:.4e}"),
+            "ratio_per_tensor_over_block": round(r["per_tensor"] / r["block_rotated"], 3),
+            "rmse_bf16_path": float(f"{r['bf16_path']:.4e}"),
+            "block_rotated_lower": bool(r["block_rotated"] < r["per_tensor"])}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -616,6 +660,8 @@ def main():
         host_out = {n: tuple(t[0].float().cpu().numpy() for t in ts)
                     for n, ts in leg_outputs.items() if n in {l["name"] for l in legs}}
         out["cpu_baseline"] = cpu_baseline({l["name"] for l in legs}, args.cpu_budget, host_out)
+        if "fwd_fp8" in {l["name"] for l in legs}:
+            out["cpu_baseline"]["fp8_accuracy"] = fp8_accuracy(fa, torch, dev)
     print(json.dumps(out), flush=True)
 
 
