@@ -11,8 +11,9 @@
 //   code  = e4m3_rne(clamp(x' / scale, -448, 448)),  stored = scale * scale_mul
 //
 // A block is FA_FP8_BLOCK = 128 rows of one (b, h), all d columns.  Each row is
-// held by d/8 consecutive lanes, 8 elements per lane; butterflies of
-// half-width < 8 stay inside a lane, wider ones pair lane t with lane t ^ (h/8).
+// held by d/16 consecutive lanes, 16 elements per lane; butterflies of
+// half-width < 16 stay inside a lane, wider ones pair lane t with lane
+// t ^ (h/16).
 #include <type_traits>
 
 #include "common.h"
@@ -23,7 +24,15 @@ namespace fa {
 namespace {
 
 constexpr int kBlock = 128;
-constexpr int kThreads = 1024;
+constexpr int kEl = 16;  // elements per lane: 16 consecutive of one row
+// Threads per workgroup: one per 16-element chunk of the block, at most 1024.
+// (Workgroups of 256 or 512 threads, with more chunks per thread, measured
+// faster only for some modes and head dimensions.)
+template <int D>
+constexpr int quant_threads() {
+  return kBlock * (D / kEl) < 1024 ? kBlock * (D / kEl) : 1024;
+}
+constexpr int kReduceThreads = 1024;
 
 template <int DT> __device__ __forceinline__ float elem_to_f32(uint32_t bits16);
 template <> __device__ __forceinline__ float elem_to_f32<0>(uint32_t b) {
@@ -33,34 +42,36 @@ template <> __device__ __forceinline__ float elem_to_f32<1>(uint32_t b) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
 }
 
-// Value of the lane `hl` away inside a 16-lane row (hl = 1, 2, 4, 8) by data
-// parallel primitives (no LDS traffic): quad permutations for 1 and 2, row
-// shifts for 4 and 8 (a lane whose bit hl is clear reads lane + hl, one whose
-// bit is set reads lane - hl).
+// Value of the lane `hl` away inside a 16-lane row (hl = 4, 8) by data
+// parallel row shifts (no LDS traffic): a lane whose bit hl is clear reads
+// lane + hl, one whose bit is set reads lane - hl.
 template <int HL>
 __device__ __forceinline__ float lane_xor_in_row(float v, bool upper) {
   const int b = __builtin_bit_cast(int, v);
-  if constexpr (HL == 1) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false));
-  } else if constexpr (HL == 2) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, false));
-  } else {
-    const int from_above = __builtin_amdgcn_update_dpp(0, b, 0x100 + HL, 0xF, 0xF, false);
-    const int from_below = __builtin_amdgcn_update_dpp(0, b, 0x110 + HL, 0xF, 0xF, false);
-    return __builtin_bit_cast(float, upper ? from_below : from_above);
-  }
+  const int from_above = __builtin_amdgcn_update_dpp(0, b, 0x100 + HL, 0xF, 0xF, false);
+  const int from_below = __builtin_amdgcn_update_dpp(0, b, 0x110 + HL, 0xF, 0xF, false);
+  return __builtin_bit_cast(float, upper ? from_below : from_above);
+}
+// Value of the lane `hl` away for hl = 1, 2: a quad permutation.
+template <int HL>
+__device__ __forceinline__ float lane_xor_in_quad(float v) {
+  constexpr int ctrl = HL == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, 0xF,
+                                                        0xF, false));
 }
 
 // MODE 0: block scales, quantise.  MODE 1: write the block amax only.
 // MODE 2: quantise with the amax found in scales[slot] (per-tensor mode).
 template <int D, int DT, int MODE>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(quant_threads<D>())
 quant_kernel(QuantArgs a) {
-  constexpr int TPR = D / 8;               // lanes per row
-  constexpr int TASKS = kBlock * TPR;      // 8-element chunks per block
-  static_assert(TASKS % kThreads == 0, "");
-  constexpr int CPT = TASKS / kThreads;
-  static_assert(TPR <= 64, "");
+  constexpr int NT = quant_threads<D>();
+  constexpr int TPR = D / kEl;             // lanes per row (4, 8 or 16)
+  constexpr int TASKS = kBlock * TPR;      // 16-element chunks per block
+  static_assert(TASKS % NT == 0, "");
+  constexpr int CPT = TASKS / NT;
+  static_assert(TPR >= 2 && TPR <= 16, "cross-lane levels stay inside a 16-lane row");
 
   const int tid = threadIdx.x;
   const int slot = blockIdx.x;             // (b*H + h) * nblk + blk
@@ -70,29 +81,33 @@ quant_kernel(QuantArgs a) {
   const int row0 = blk * kBlock;
   const int64_t base = (int64_t)bh * N * D;
 
-  float x[CPT][8];
+  float x[CPT][kEl];
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int c = tid + i * kThreads;
+    const int c = tid + i * NT;
     const int r = c / TPR;
-    const int col = (c % TPR) * 8;
+    const int col = (c % TPR) * kEl;
     const int row = row0 + r;
-    u32x4_t raw = {0u, 0u, 0u, 0u};
-    if (row < N) raw = ld_global16(static_cast<const uint16_t*>(a.x) + base + (int64_t)row * D + col);
+    u32x4_t raw[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    if (row < N) {
+      const uint16_t* src = static_cast<const uint16_t*>(a.x) + base + (int64_t)row * D + col;
+      raw[0] = ld_global16(src);
+      raw[1] = ld_global16(src + 8);
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[i][2 * j] = elem_to_f32<DT>(raw[j] & 0xffffu);
-      x[i][2 * j + 1] = elem_to_f32<DT>(raw[j] >> 16);
+    for (int j = 0; j < 8; ++j) {
+      x[i][2 * j] = elem_to_f32<DT>(raw[j >> 2][j & 3] & 0xffffu);
+      x[i][2 * j + 1] = elem_to_f32<DT>(raw[j >> 2][j & 3] >> 16);
     }
     if (a.signs != nullptr) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[i][e] *= a.signs[col + e];
-      // Half-widths 1, 2, 4: inside the lane.
+      for (int e = 0; e < kEl; ++e) x[i][e] *= a.signs[col + e];
+      // Half-widths 1, 2, 4, 8: inside the lane.
 #pragma unroll
-      for (int h = 1; h < 8; h <<= 1) {
+      for (int h = 1; h < kEl; h <<= 1) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < kEl; ++e) {
           if ((e & h) == 0) {
             const float lo = x[i][e], hi = x[i][e + h];
             x[i][e] = lo + hi;
@@ -100,33 +115,35 @@ quant_kernel(QuantArgs a) {
           }
         }
       }
-      // Half-widths 8 .. D/2: partner lane t ^ (h/8) within the row's lanes
-      // (inside a 16-lane row by data-parallel moves, across rows by a lane
-      // shuffle).
+      // Half-widths 16 .. D/2: partner lane t ^ (h/16) of the row's lanes, by
+      // data-parallel moves.  The lower lane of a pair keeps mine + other,
+      // the upper one other - mine; for the quad permutations as one fused
+      // multiply-add with +-1, which rounds exactly like the sum or the
+      // difference.
       const int t = c % TPR;
       auto level = [&](auto hl_tag) {
         constexpr int HL = decltype(hl_tag)::value;
         const bool upper = (t & HL) != 0;
+        const float sgn = upper ? -1.0f : 1.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < kEl; ++e) {
           const float mine = x[i][e];
-          float other;
-          if constexpr (HL < 16)
-            other = lane_xor_in_row<HL>(mine, upper);
-          else
-            other = __shfl_xor(mine, HL, TPR);
-          x[i][e] = upper ? (other - mine) : (mine + other);
+          if constexpr (HL < 4) {
+            x[i][e] = fmaf(sgn, mine, lane_xor_in_quad<HL>(mine));
+          } else {
+            const float other = lane_xor_in_row<HL>(mine, upper);
+            x[i][e] = upper ? (other - mine) : (mine + other);
+          }
         }
       };
-      if constexpr (TPR > 1) level(std::integral_constant<int, 1>{});
-      if constexpr (TPR > 2) level(std::integral_constant<int, 2>{});
+      level(std::integral_constant<int, 1>{});
+      level(std::integral_constant<int, 2>{});
       if constexpr (TPR > 4) level(std::integral_constant<int, 4>{});
       if constexpr (TPR > 8) level(std::integral_constant<int, 8>{});
-      if constexpr (TPR > 16) level(std::integral_constant<int, 16>{});
     }
     if (row < N) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
+      for (int e = 0; e < kEl; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
     }
   }
 
@@ -134,15 +151,15 @@ quant_kernel(QuantArgs a) {
   if (MODE == 2) {
     block_amax = a.scales[slot];
   } else {
-    // Workgroup max: wave reduction, then across the 16 waves through LDS.
-    __shared__ float red[kThreads / 64];
+    // Workgroup max: wave reduction, then across the waves through LDS.
+    __shared__ float red[NT / 64];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
     if ((tid & 63) == 0) red[tid >> 6] = amax;
     __syncthreads();
     block_amax = red[0];
 #pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) block_amax = fmaxf(block_amax, red[w]);
+    for (int w = 1; w < NT / 64; ++w) block_amax = fmaxf(block_amax, red[w]);
     if (MODE == 1) {
       if (tid == 0) a.scales[slot] = block_amax;
       return;
@@ -162,14 +179,14 @@ quant_kernel(QuantArgs a) {
   };
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int c = tid + i * kThreads;
+    const int c = tid + i * NT;
     const int r = c / TPR;
-    const int col = (c % TPR) * 8;
+    const int col = (c % TPR) * kEl;
     const int row = row0 + r;
     if (row >= N) continue;
-    u32x2_t out;
+    u32x4_t out;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 4; ++j) {
       float y[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -178,27 +195,27 @@ quant_kernel(QuantArgs a) {
       w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
       out[j] = (uint32_t)w;
     }
-    *reinterpret_cast<u32x2_t*>(static_cast<uint8_t*>(a.x8) + base + (int64_t)row * D + col) = out;
+    *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(a.x8) + base + (int64_t)row * D + col) = out;
   }
   if (MODE == 2) __syncthreads();  // every lane has read scales[slot]
   if (tid == 0) a.scales[slot] = scale * a.scale_mul;
 }
 
 // Max over n values, written back to all n (one workgroup).
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kReduceThreads)
 reduce_max_kernel(float* v, int n) {
-  __shared__ float red[kThreads / 64];
+  __shared__ float red[kReduceThreads / 64];
   float m = 0.f;
-  for (int i = threadIdx.x; i < n; i += kThreads) m = fmaxf(m, v[i]);
+  for (int i = threadIdx.x; i < n; i += kReduceThreads) m = fmaxf(m, v[i]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   m = red[0];
 #pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, red[w]);
+  for (int w = 1; w < kReduceThreads / 64; ++w) m = fmaxf(m, red[w]);
   __syncthreads();
-  for (int i = threadIdx.x; i < n; i += kThreads) v[i] = m;
+  for (int i = threadIdx.x; i < n; i += kReduceThreads) v[i] = m;
 }
 
 template <int D, int DT>
@@ -206,16 +223,19 @@ hipError_t launch_d(const QuantArgs& a, int BH, bool per_tensor, hipStream_t s) 
   const int64_t grid = (int64_t)BH * a.nblk;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (!per_tensor) {
-    hipLaunchKernelGGL((quant_kernel<D, DT, 0>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((quant_kernel<D, DT, 0>), dim3((unsigned)grid), dim3(quant_threads<D>()), 0,
+                       s, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((quant_kernel<D, DT, 1>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((quant_kernel<D, DT, 1>), dim3((unsigned)grid), dim3(quant_threads<D>()), 0, s,
+                     a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(reduce_max_kernel, dim3(1), dim3(kThreads), 0, s, a.scales, (int)grid);
+  hipLaunchKernelGGL(reduce_max_kernel, dim3(1), dim3(kReduceThreads), 0, s, a.scales, (int)grid);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((quant_kernel<D, DT, 2>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((quant_kernel<D, DT, 2>), dim3((unsigned)grid), dim3(quant_threads<D>()), 0, s,
+                     a);
   return hipGetLastError();
 }
 
