@@ -35,8 +35,12 @@ the host cores.  The oracle leg also scores the FP8 path (block scales and
 rotation) against per-tensor-scaled FP8 on the FP8 workload's outlier-injected
 inputs (cpu_baseline.fp8_accuracy: RMSE of four heads against the oracle).
 
+``--sweep`` instead times every benchmark configuration (the forward sweep
+at N = 2k-16k, the long-context head dimensions, fp8, the backward), one JSON
+line each.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                      [--no-next-rows]
+                      [--no-next-rows] [--sweep]
 """
 
 from __future__ import annotations
@@ -492,6 +496,94 @@ def fp8_accuracy(fa, torch, dev):
             "block_rotated_lower": bool(r["block_rotated"] < r["per_tensor"])}
 
 
+def sweep(torch, fa, dev, rounds=3, calls=10):
+    """Time every benchmark configuration (one JSON line each): the bf16
+    forward sweep at B*N = 16384 (N = 2k, 4k, 8k) causal and not, the
+    long-context causal forward at N = 16384 for d = 64 / 128 / 256, the fp8
+    forward (+ its quantisation) at B=4, N=4096 and B=2, N=8192 on outlier
+    inputs, and the bf16 backward at B=4, N=4096; plus the tiny B=1, H=2,
+    N=256, d=64 case (launch-bound).  Inputs are seeded N(0,1) draws (device
+    RNG; the fp8 cases use the seeded host outlier inputs); each entry is
+    the median over `rounds` of `calls` back-to-back launches."""
+    from exact_tiled_attention_16_amd import inputs
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2024)
+
+    def randn(*shape):
+        return torch.randn(*shape, device=dev, generator=gen).to(torch.bfloat16)
+
+    def timed(call):
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(rounds):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(calls):
+                call()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / calls)
+        return sorted(ts)[len(ts) // 2]
+
+    def emit(name, op, B, H, N, d, causal, ms, flop, dtype, extra=None):
+        tf = flop / (ms * 1e-3) / 1e12
+        rec = {"sweep": name, "op": op, "B": B, "H": H, "N": N, "d": d, "causal": causal,
+               "ms": round(ms, 4), "tflops": round(tf, 1),
+               "frac_of_peak": round(tf / PEAK_TFLOPS[dtype], 4), "dtype": dtype}
+        if extra:
+            rec.update(extra)
+        print(json.dumps(rec), flush=True)
+
+    def fwd_case(name, B, H, N, d, causal):
+        q, k, v = randn(B, H, N, d), randn(B, H, N, d), randn(B, H, N, d)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        ms = timed(lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse))
+        emit(name, "fwd", B, H, N, d, causal, ms, fwd_flops(B, H, N, d, causal), "bf16")
+
+    fwd_case("tiny", 1, 2, 256, 64, False)
+    fwd_case("tiny", 1, 2, 256, 64, True)
+    for B, N in ((8, 2048), (4, 4096), (2, 8192)):
+        for causal in (False, True):
+            fwd_case("bf16 forward sweep", B, 16, N, 128, causal)
+    for H, d in ((16, 128), (32, 64), (8, 256)):
+        fwd_case("long-context forward", 1, H, 16384, d, True)
+
+    for B, N in ((4, 4096), (2, 8192)):
+        H, d = 16, 128
+        host = [torch.from_numpy(x).to(torch.bfloat16) for x in inputs.qkv_outliers(B, H, N, d, 4)]
+        qd, kd, vd = (t.to(dev) for t in host)
+        del host
+        sg = torch.from_numpy(inputs.signs(d, 4)).to(dev)
+        q8, qs = fa.quant_fp8(qd, signs=sg, scale_mul=1.0 / d)
+        k8, ks = fa.quant_fp8(kd, signs=sg)
+        v8, vs = fa.quant_fp8(vd)
+        ms_q = timed(lambda: (fa.quant_fp8(qd, signs=sg, scale_mul=1.0 / d, out=q8, scales=qs),
+                              fa.quant_fp8(kd, signs=sg, out=k8, scales=ks),
+                              fa.quant_fp8(vd, out=v8, scales=vs)))
+        o = torch.empty_like(qd)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        for causal in (False, True):
+            ms = timed(lambda: fa.fwd_fp8(q8, k8, v8, qs, ks, vs, causal=causal, out=o, lse=lse))
+            emit("fp8 forward", "fwd_fp8", B, H, N, d, causal, ms, fwd_flops(B, H, N, d, causal),
+                 "fp8", {"quant_fp8_ms_qkv": round(ms_q, 4)})
+        del qd, kd, vd, q8, k8, v8
+
+    B, H, N, d = 4, 16, 4096, 128
+    q, k, v, do = (randn(B, H, N, d) for _ in range(4))
+    dq = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    dk, dv = torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(max(fa.fa_bwd_workspace_size(B, H, N, d), 16), dtype=torch.uint8, device=dev)
+    for causal in (True, False):
+        o, lse = fa.fwd(q, k, v, causal=causal)
+        ms = timed(lambda: fa.bwd(q, k, v, o, lse, do, causal=causal, dq=dq, dk=dk, dv=dv,
+                                  workspace=ws))
+        emit("bf16 backward", "bwd", B, H, N, d, causal, ms,
+             2.5 * fwd_flops(B, H, N, d, causal), "bf16")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -501,6 +593,9 @@ def main():
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip the rows beyond the hot path")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the step: time every benchmark configuration "
+                         "(one JSON line each)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one device copy of this many MiB "
                          "(reference kernel for the traffic counters)")
@@ -519,6 +614,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     fa.lib()
+    if args.sweep:
+        sweep(torch, fa, dev)
+        return
     legs_all, fwd_inputs, leg_outputs = build_legs(torch, fa, dev)
     torch.cuda.synchronize()
 
