@@ -391,11 +391,22 @@ def cpu_baseline(legs_present, budget_s=15.0, gpu_out=None):
     from exact_tiled_attention_16_amd import inputs
     from oracle import attention as oatt
     from oracle import fp8 as ofp8
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        threads = max((i.get("num_threads", 1) for i in pools), default=1)
+        if pools:
+            blas = f"{pools[0].get('internal_api', '?')} {pools[0].get('version', '')}".strip()
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")),
+                             None)
+    except OSError:  # pragma: no cover
+        pass
     B, H, N, d = (WORKLOAD[k] for k in "BHNd")
     def bf16(x):
         return torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
@@ -448,7 +459,9 @@ def cpu_baseline(legs_present, budget_s=15.0, gpu_out=None):
         verify = {"heads": heads, "pass": bool(ok),
                   **{key: float(f"{v:.3e}") for key, v in err.items()}}
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "verify_timed_outputs": verify,
+            "kind": "oracle", "cpu_model": cpu_model, "blas": blas,
+            "affinity_cpus": len(os.sched_getaffinity(0)),
+            "verify_timed_outputs": verify,
             "sample": f"fp64 numpy oracle, legs {sorted(legs_present)}, {heads} of "
                       f"{B * H} heads (b=0, h<{heads}) of B={B},H={H},N={N},d={d}, "
                       f"{dt:.1f} s wall"}
