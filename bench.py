@@ -517,10 +517,17 @@ def sweep(torch, fa, dev, rounds=3, calls=10):
     inputs, and the bf16 backward at B=4, N=4096; plus the tiny B=1, H=2,
     N=256, d=64 case (launch-bound).  Inputs are seeded N(0,1) draws (device
     RNG; the fp8 cases use the seeded host outlier inputs); each entry is
-    the median over `rounds` of `calls` back-to-back launches."""
+    the median over `rounds` of `calls` back-to-back launches through the raw
+    entry points (device pointers and sizes prepared once, so the host
+    enqueues faster than the kernels run)."""
     from exact_tiled_attention_16_amd import inputs
     gen = torch.Generator(device=dev)
     gen.manual_seed(2024)
+    st = torch.cuda.current_stream(dev).cuda_stream
+
+    def ok(rc):
+        if rc != fa.FA_OK:
+            raise fa.FaError(rc)
 
     def randn(*shape):
         return torch.randn(*shape, device=dev, generator=gen).to(torch.bfloat16)
@@ -553,8 +560,24 @@ def sweep(torch, fa, dev, rounds=3, calls=10):
         q, k, v = randn(B, H, N, d), randn(B, H, N, d), randn(B, H, N, d)
         o = torch.empty_like(q)
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-        ms = timed(lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse))
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                B, H, N, d, fa.FA_BF16, 1.0 / math.sqrt(d), int(causal), st)
+        ok(fa.fa_fwd(*args))
+        ms = timed(lambda: fa.fa_fwd(*args))
         emit(name, "fwd", B, H, N, d, causal, ms, fwd_flops(B, H, N, d, causal), "bf16")
+
+    # Bring the clocks up before the first measurement: ~0.3 s of forwards.
+    wq = randn(2, 16, 8192, 128)
+    wo = torch.empty_like(wq)
+    wl = torch.empty((2, 16, 8192), dtype=torch.float32, device=dev)
+    wargs = (wq.data_ptr(), wq.data_ptr(), wq.data_ptr(), wo.data_ptr(), wl.data_ptr(),
+             2, 16, 8192, 128, fa.FA_BF16, 1.0 / math.sqrt(128), 0, st)
+    t_end = time.perf_counter() + 0.3
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            ok(fa.fa_fwd(*wargs))
+        torch.cuda.synchronize()
+    del wq, wo, wl
 
     fwd_case("tiny", 1, 2, 256, 64, False)
     fwd_case("tiny", 1, 2, 256, 64, True)
@@ -573,13 +596,20 @@ def sweep(torch, fa, dev, rounds=3, calls=10):
         q8, qs = fa.quant_fp8(qd, signs=sg, scale_mul=1.0 / d)
         k8, ks = fa.quant_fp8(kd, signs=sg)
         v8, vs = fa.quant_fp8(vd)
-        ms_q = timed(lambda: (fa.quant_fp8(qd, signs=sg, scale_mul=1.0 / d, out=q8, scales=qs),
-                              fa.quant_fp8(kd, signs=sg, out=k8, scales=ks),
-                              fa.quant_fp8(vd, out=v8, scales=vs)))
+        qa = (qd.data_ptr(), fa.FA_BF16, q8.data_ptr(), qs.data_ptr(), sg.data_ptr(), 1.0 / d, 0,
+              B, H, N, d, st)
+        ka = (kd.data_ptr(), fa.FA_BF16, k8.data_ptr(), ks.data_ptr(), sg.data_ptr(), 1.0, 0,
+              B, H, N, d, st)
+        va = (vd.data_ptr(), fa.FA_BF16, v8.data_ptr(), vs.data_ptr(), None, 1.0, 0, B, H, N, d, st)
+        ms_q = timed(lambda: (fa.fa_quant_fp8(*qa), fa.fa_quant_fp8(*ka), fa.fa_quant_fp8(*va)))
         o = torch.empty_like(qd)
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
         for causal in (False, True):
-            ms = timed(lambda: fa.fwd_fp8(q8, k8, v8, qs, ks, vs, causal=causal, out=o, lse=lse))
+            fargs = (q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), qs.data_ptr(), ks.data_ptr(),
+                     vs.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d, 1.0 / math.sqrt(d),
+                     int(causal), st)
+            ok(fa.fa_fwd_fp8(*fargs))
+            ms = timed(lambda: fa.fa_fwd_fp8(*fargs))
             emit("fp8 forward", "fwd_fp8", B, H, N, d, causal, ms, fwd_flops(B, H, N, d, causal),
                  "fp8", {"quant_fp8_ms_qkv": round(ms_q, 4)})
         del qd, kd, vd, q8, k8, v8
@@ -591,8 +621,11 @@ def sweep(torch, fa, dev, rounds=3, calls=10):
     ws = torch.empty(max(fa.fa_bwd_workspace_size(B, H, N, d), 16), dtype=torch.uint8, device=dev)
     for causal in (True, False):
         o, lse = fa.fwd(q, k, v, causal=causal)
-        ms = timed(lambda: fa.bwd(q, k, v, o, lse, do, causal=causal, dq=dq, dk=dk, dv=dv,
-                                  workspace=ws))
+        bargs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
+                 B, H, N, d, fa.FA_BF16, 1.0 / math.sqrt(d), int(causal), st)
+        ok(fa.fa_bwd(*bargs))
+        ms = timed(lambda: fa.fa_bwd(*bargs))
         emit("bf16 backward", "bwd", B, H, N, d, causal, ms,
              2.5 * fwd_flops(B, H, N, d, causal), "bf16")
 
