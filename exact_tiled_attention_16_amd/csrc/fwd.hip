@@ -483,11 +483,15 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
         int lim = kn - t * BN - 4 * hl;
         if (CAUSAL) lim = min(lim, qw0 + 32 * qb + l32 + 1 + coff - t * BN - 4 * hl);
         if (dead) lim = -BN;
+        // Tiles of the masked tail that need no mask in any lane skip it.
+        constexpr int kMaxOff = (NKB - 1) * 32 + 27;  // largest key offset of a register
+        if (wave_any(lim <= kMaxOff)) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+          for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s_nxt[qb][kb][r] = -INFINITY;
+            for (int r = 0; r < 16; ++r)
+              if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s_nxt[qb][kb][r] = -INFINITY;
+        }
       }
     }
     if constexpr (DP) {

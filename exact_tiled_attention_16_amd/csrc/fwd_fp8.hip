@@ -443,11 +443,15 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
       const int t = j + 1;
       int lim = N - t * BN - 4 * hl;
       if (CAUSAL) lim = min(lim, qrow + 1 - t * BN - 4 * hl);
+      // Tiles of the masked tail that need no mask in any lane skip it.
+      constexpr int kMaxOff = (NKB - 1) * 32 + 27;  // largest key offset of a register
+      if (wave_any(lim <= kMaxOff)) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s_nxt[kb][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r)
+            if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s_nxt[kb][r] = -INFINITY;
+      }
     }
     if constexpr (DP) finish_tile(s_cur, p_cur, mul, ps0 + ps1, vs_j);
     if constexpr (!GROUPED)
