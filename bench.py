@@ -467,6 +467,22 @@ def cpu_baseline(legs_present, budget_s=15.0, gpu_out=None):
                       f"{dt:.1f} s wall"}
 
 
+def mall_note(B, H, N, d):
+    """Cache state the legs start in: a step's working set against the
+    MI355X's 256 MiB Infinity Cache (MALL)."""
+    t = B * H * N * d                       # elements per tensor
+    mib = 2.0 ** 20
+    fwd = (4 * 2 * t + 4 * B * H * N) / mib                   # Q, K, V, O bf16 + LSE
+    fp8 = (3 * 2 * t + 3 * t + t + 2 * t) / mib               # quant: read bf16, write e4m3; fwd: O
+    bwd = (5 * 2 * t + 4 * t + 2 * 2 * t + 3 * 4 * B * H * N) / mib  # Q K V O dO, dQ fp32, dK dV
+    total = fwd + fp8 + bwd
+    return (f"cold between legs: one step touches ~{total:.0f} MiB "
+            f"(fwd {fwd:.0f}, fp8 {fp8:.0f}, bwd {bwd:.0f}), "
+            f"{total / 256:.1f}x the 256 MiB Infinity Cache, so each leg finds its inputs "
+            f"mostly evicted by the previous one; within a leg the K/V re-reads of one head "
+            f"hit L2 and the Infinity Cache")
+
+
 def fp8_accuracy(fa, torch, dev):
     """Error of the FP8 path with block scales and the Hadamard rotation
     against per-tensor-scaled FP8 without rotation (the same kernel), on the
@@ -783,7 +799,8 @@ def main():
         "config": {"workload": f"attention B={B} H={H} N={N} d={d} non-causal "
                                f"(bf16 forward sweep, longest sequence)",
                    "B": B, "H": H, "N": N, "d": d, "causal": False,
-                   "legs": [l["name"] for l in legs], "legs_missing": missing},
+                   "legs": [l["name"] for l in legs], "legs_missing": missing,
+                   "mall": mall_note(B, H, N, d)},
         "legs": leg_report,
         "roofline": roofline,
     }
