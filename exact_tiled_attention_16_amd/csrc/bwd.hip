@@ -363,7 +363,13 @@ bwd_kv3_kernel(BwdArgs a) {
           }
         acc_products(sb + QTB);  // dV^T += dO(i)^T P(i)
       } else {
+        // The dS' + dK phase is the critical path of a tile: it runs at raised
+        // priority, so the S side's products fill in around it (2-4 % faster
+        // than equal priorities; raising either role for the whole tile was
+        // slower at d = 128).
+        __builtin_amdgcn_s_setprio(1);
         if constexpr (!FIRST) ds_and_dk((i - 1) & 1, lds + (st == 0 ? 2 : st - 1) * STAGEB);
+        __builtin_amdgcn_s_setprio(0);
         load_stats(sb);
         row_products(sb + QTB);  // dP(i) - D, kept for the next tile
       }
