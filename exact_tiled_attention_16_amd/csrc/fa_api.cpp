@@ -43,8 +43,10 @@ const char* fa_status_str(int status) {
   }
 }
 
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
-           int d, int dtype, float scale, int causal, void* stream) {
+namespace {
+
+int fwd_entry(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+              int N, int d, int dtype, float scale, int causal, void* stream, bool per_tile) {
   if (!q || !k || !v || !o) return FA_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_INVALID;
   if (!aligned4(lse)) return FA_ERR_INVALID;
@@ -59,10 +61,26 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   a.lse = lse;
   a.N = N;
   a.scale_log2 = scale * 1.4426950408889634f;
-  return launch_status(
-      fa::launch_fwd(a, B, H, d, dtype, causal != 0, static_cast<hipStream_t>(stream)));
+  return launch_status(fa::launch_fwd(a, B, H, d, dtype, causal != 0,
+                                      static_cast<hipStream_t>(stream), per_tile));
 }
 
+}  // namespace
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, int dtype, float scale, int causal, void* stream) {
+  return fwd_entry(q, k, v, o, lse, B, H, N, d, dtype, scale, causal, stream, false);
+}
+
+// Not part of the ABI (no declaration in include/): fa_fwd with the causal
+// work dispatched as one workgroup per query tile instead of the persistent
+// schedule.  The outputs are bit-identical to fa_fwd's; the parity tests use
+// it to check that, and the benchmark to time the two schedules side by side.
+int fa_testing_fwd_per_tile(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int N, int d, int dtype, float scale, int causal,
+                            void* stream) {
+  return fwd_entry(q, k, v, o, lse, B, H, N, d, dtype, scale, causal, stream, true);
+}
 
 int fa_fwd_partial(const void* q, const void* k, const void* v, float* o, float* lse, int B,
                    int H, int Nq, int Nk, int d, int dtype, float scale, int causal, int q_pos0,
@@ -241,7 +259,7 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_sc
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
-  if (!valid_dims(B, H, N) || !supported_d(d)) return 0;
+  if (!valid_dims(B, H, N) || !supported_d(d) || !fa::bwd_supported(d)) return 0;
   return (size_t)B * H * N * 2 * sizeof(float);  // per row: LSE * log2 e, rowsum(dO o O)
 }
 

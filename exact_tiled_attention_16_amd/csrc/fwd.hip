@@ -30,7 +30,6 @@
 //     reads; O^T has one query per lane, so the rescale is a per-lane multiply.
 #include <algorithm>
 #include <atomic>
-#include <cstdlib>
 #include <type_traits>
 
 #include "common.h"
@@ -605,27 +604,15 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
 }
 
 // Per head dimension: keys per tile, waves per workgroup, query blocks per
-// wave, waves per SIMD, LDS stages per tensor.  FA_FWD128_CFG = 1 selects a
-// d = 128 layout with four-wave workgroups and two stages, so that two
-// workgroups share a CU and their barriers do not couple (measured slower
-// than the default on MI355X; kept for comparison).
+// wave, waves per SIMD, LDS stages per tensor.
 template <int D> struct FwdCfg;
-#ifndef FA_FWD128_CFG
-#define FA_FWD128_CFG 0
-#endif
 // d = 64 runs its iterations in pairs with one barrier per pair (four
 // stages, 64 KiB of LDS): 1.3 % faster than a barrier per tile; at d = 128
-// (128 KiB) that was 1 % slower than three stages.
+// (128 KiB) that was 1 % slower than three stages.  Four-wave workgroups at
+// d = 128 (two per CU, or one wave per SIMD with 64 query rows per wave)
+// measured slower than eight waves with two per SIMD.
 template <> struct FwdCfg<64> { static constexpr int BN = 64, NW = 8, QB = 1, OCC = 2, NSTG = 4; };
-#if FA_FWD128_CFG == 1
-template <> struct FwdCfg<128> { static constexpr int BN = 64, NW = 4, QB = 1, OCC = 2, NSTG = 2; };
-#elif FA_FWD128_CFG == 2
-template <> struct FwdCfg<128> { static constexpr int BN = 64, NW = 4, QB = 1, OCC = 1, NSTG = 3; };
-#elif FA_FWD128_CFG == 3
-template <> struct FwdCfg<128> { static constexpr int BN = 64, NW = 4, QB = 2, OCC = 1, NSTG = 3; };
-#else
 template <> struct FwdCfg<128> { static constexpr int BN = 64, NW = 8, QB = 1, OCC = 2, NSTG = 3; };
-#endif
 template <> struct FwdCfg<256> { static constexpr int BN = 32, NW = 4, QB = 1, OCC = 1, NSTG = 3; };
 
 // Partial (split-KV) calls with at most kNarrowRows query rows -- decoding --
@@ -705,23 +692,23 @@ hipError_t launch_one(const FwdArgs& a, int BH, hipStream_t stream,
   return hipGetLastError();
 }
 
-// Causal schedule: FA_FWD_SCHED=1 gives one workgroup per query tile in
-// dispatch order (heaviest tile of each head first), anything else the
-// persistent schedule.
+// Causal schedule: the persistent heaviest-first grid, or (per_tile) one
+// workgroup per query tile in dispatch order, heaviest tile of each head
+// first.  Both produce bit-identical outputs.
 template <int D, int DT>
-hipError_t launch_causal(const FwdArgs& a, int BH, bool causal, hipStream_t s) {
+hipError_t launch_causal(const FwdArgs& a, int BH, bool causal, bool per_tile, hipStream_t s) {
   if (!causal) return launch_one<D, false, false, false, DT>(a, BH, s);
-  const char* e = std::getenv("FA_FWD_SCHED");
-  if (e != nullptr && std::atoi(e) == 1) return launch_one<D, true, false, false, DT>(a, BH, s);
+  if (per_tile) return launch_one<D, true, false, false, DT>(a, BH, s);
   return launch_one<D, true, true, false, DT>(a, BH, s);
 }
 
 template <int DT>
-hipError_t launch_dtype(const FwdArgs& a, int BH, int d, bool causal, hipStream_t s) {
+hipError_t launch_dtype(const FwdArgs& a, int BH, int d, bool causal, bool per_tile,
+                        hipStream_t s) {
   switch (d) {
-    case 64: return launch_causal<64, DT>(a, BH, causal, s);
-    case 128: return launch_causal<128, DT>(a, BH, causal, s);
-    case 256: return launch_causal<256, DT>(a, BH, causal, s);
+    case 64: return launch_causal<64, DT>(a, BH, causal, per_tile, s);
+    case 128: return launch_causal<128, DT>(a, BH, causal, per_tile, s);
+    case 256: return launch_causal<256, DT>(a, BH, causal, per_tile, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -853,15 +840,15 @@ hipError_t launch_fwd_sparse(const FwdArgs& a0, int B, int H, int d, int dtype, 
 }
 
 hipError_t launch_fwd(const FwdArgs& a0, int B, int H, int d, int dtype, bool causal,
-                      hipStream_t stream) {
+                      hipStream_t stream, bool per_tile) {
   FwdArgs a = a0;
   a.Nk = a.N;  // every key, one split, top-left diagonal
   a.c_off = 0;
   a.k_chunk = a.N;
   a.n_split = 1;
   const int BH = B * H;
-  return dtype == 0 ? launch_dtype<0>(a, BH, d, causal, stream)
-                    : launch_dtype<1>(a, BH, d, causal, stream);
+  return dtype == 0 ? launch_dtype<0>(a, BH, d, causal, per_tile, stream)
+                    : launch_dtype<1>(a, BH, d, causal, per_tile, stream);
 }
 
 hipError_t launch_fwd_partial(const FwdArgs& a, int B, int H, int d, int dtype, bool causal,

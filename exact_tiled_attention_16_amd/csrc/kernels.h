@@ -35,8 +35,11 @@ struct FwdArgs {
 constexpr int kSparseBlock = 128;
 
 // Enqueue the 16-bit forward.  Arguments are validated by the caller.
+// per_tile selects, for causal calls, one workgroup per query tile in
+// dispatch order instead of the persistent schedule (same outputs bit for
+// bit; a comparison aid).
 hipError_t launch_fwd(const FwdArgs& a, int B, int H, int d, int dtype, bool causal,
-                      hipStream_t stream);
+                      hipStream_t stream, bool per_tile = false);
 
 // Enqueue the split-KV partial forward (fp32 partial outputs per split).
 hipError_t launch_fwd_partial(const FwdArgs& a, int B, int H, int d, int dtype, bool causal,
@@ -69,7 +72,7 @@ struct BwdArgs {
   const float* lse;
   float* dsum;       // workspace: two planes of B*H*N floats, -LSE/scale then -rowsum(dO o O)
   int64_t plane;     // B*H*N, filled in by the launcher
-  float* dq;         // fp32 [B][H][N][d], zeroed by the preprocess kernel
+  float* dq;         // fp32 [B][H][N][d], written once per row by the dQ kernel
   void* dk;
   void* dv;
   int N;

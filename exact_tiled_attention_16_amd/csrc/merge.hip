@@ -5,10 +5,11 @@
 // log-sum-exp L_p, and the whole is
 //     L = log sum_p exp(L_p),    O = sum_p exp(L_p - L) O_p,
 // the same rescaling that the online softmax applies from one key tile to the
-// next ("FlashAttention-3: Fast and Accurate Attention with Asynchrony and
-// Low-precision", the online-softmax description; its reference list names
-// Ring Attention and Lean Attention, which combine per-device and per-split
-// partial results this way).  A part with no visible key has L_p = -inf and
+// next (FlashAttention-4 related-papers page, online-softmax snippet: a
+// running maximum and normaliser).  The reference list of "FlashAttention-3:
+// Fast and Accurate Attention with Asynchrony and Low-precision" names Ring
+// Attention and Lean Attention, which combine per-device and per-split
+// partial results this way.  A part with no visible key has L_p = -inf and
 // weight 0; a row with no visible key anywhere gets O = 0 and L = -inf.
 //
 // Memory-bound: one pass over the partial outputs.  D/4 lanes per row, each

@@ -50,6 +50,12 @@ SIGNATURES = {
                                 _F, _I, _P]),
     "fa_status_str": (ctypes.c_char_p, [_I]),
 }
+# Exported by libfa.so but not part of the C ABI (no declaration in
+# include/): fa_fwd with the causal work dispatched as one workgroup per query
+# tile instead of the persistent schedule, for comparing the two.
+INTERNAL_SIGNATURES = {
+    "fa_testing_fwd_per_tile": SIGNATURES["fa_fwd"],
+}
 
 _lib = None
 
@@ -62,7 +68,7 @@ def lib() -> ctypes.CDLL:
             raise OSError(f"{LIB_PATH} is missing; run "
                           "`python -m exact_tiled_attention_16_amd.build`")
         l = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
+        for name, (res, args) in {**SIGNATURES, **INTERNAL_SIGNATURES}.items():
             fn = getattr(l, name)
             fn.restype = res
             fn.argtypes = args
@@ -90,6 +96,12 @@ def _check(code: int) -> None:
 def fa_fwd(q, k, v, o, lse, B, H, N, d, dtype, scale, causal, stream) -> int:
     return lib().fa_fwd(q, k, v, o, lse, B, H, N, d, dtype, scale, causal,
                         stream)
+
+
+def fa_testing_fwd_per_tile(q, k, v, o, lse, B, H, N, d, dtype, scale, causal,
+                            stream) -> int:
+    return lib().fa_testing_fwd_per_tile(q, k, v, o, lse, B, H, N, d, dtype,
+                                         scale, causal, stream)
 
 
 def fa_quant_fp8(x, dtype, x8, scales, signs, scale_mul, per_tensor, B, H, N,
@@ -178,8 +190,12 @@ def _stream(t) -> int:
 
 
 def fwd(q, k, v, causal: bool = False, scale: float | None = None,
-        out=None, lse=None):
-    """O, LSE = attention(q, k, v) for [B, H, N, d] bf16/fp16 device tensors."""
+        out=None, lse=None, per_tile: bool = False):
+    """O, LSE = attention(q, k, v) for [B, H, N, d] bf16/fp16 device tensors.
+
+    per_tile=True dispatches causal work as one workgroup per query tile
+    (fa_testing_fwd_per_tile) instead of the persistent schedule; the outputs
+    are the same bit for bit."""
     torch = _torch()
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d]")
@@ -195,9 +211,10 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None,
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check_tensor(lse, "lse", (B, H, N), torch.float32)
-    _check(fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                  lse.data_ptr(), B, H, N, d, dt, float(scale), int(bool(causal)),
-                  _stream(q)))
+    entry = fa_testing_fwd_per_tile if per_tile else fa_fwd
+    _check(entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                 lse.data_ptr(), B, H, N, d, dt, float(scale), int(bool(causal)),
+                 _stream(q)))
     return out, lse
 
 

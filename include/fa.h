@@ -33,7 +33,9 @@
  * Errors.  Argument problems are reported synchronously, before anything is
  * enqueued: FA_ERR_INVALID for null pointers, non-positive sizes, unknown
  * dtype, misaligned pointers or a non-finite or non-positive scale;
- * FA_ERR_UNSUPPORTED for a head dimension other than 64, 128 or 256.
+ * FA_ERR_UNSUPPORTED for a head dimension other than 64, 128 or 256 (and,
+ * for fa_bwd and fa_bwd_workspace_size, for d = 256: the backward is built
+ * for d = 64 and 128 only).
  * FA_ERR_LAUNCH means the HIP runtime refused a kernel launch.  Faults inside
  * a kernel surface at the caller's next synchronisation.
  */
@@ -105,7 +107,12 @@ int fa_quant_fp8(const void* x, int dtype, void* x8, float* scales,
                  int B, int H, int N, int d, void* stream);
 
 /*
- * fa_fwd_fp8 -- attention forward on e4m3 operands.
+ * fa_fwd_fp8 -- attention forward on e4m3 operands: the FP8 variant of the
+ * same exact attention, with one scale per block of rows instead of per
+ * tensor and incoherent processing of Q and K ("FlashAttention-3: Fast and
+ * Accurate Attention with Asynchrony and Low-precision", abstract and core
+ * claim: block quantization and incoherent processing on hardware FP8
+ * support).  The block scales and the rotation come from fa_quant_fp8.
  *   q8, k8, v8        : [B][H][N][d] e4m3 codes from fa_quant_fp8 (Q and K
  *                       rotated with the same signs, Q with scale_mul 1/d).
  *   q_scale, k_scale,
@@ -113,10 +120,14 @@ int fa_quant_fp8(const void* x, int dtype, void* x8, float* scales,
  *   o                 : [B][H][N][d] bf16, written.
  *   lse               : [B][H][N] float or NULL, as in fa_fwd.
  *   scale, causal     : as in fa_fwd (the ordinary softmax scale).
+ *   Errors            : as in fa_fwd (no dtype argument: the codes are
+ *                       e4m3, the output bf16).
  * S = Q8 K8^T runs on fp8 matrix-core instructions with fp32 accumulation;
  * block scales are folded into the fp32 scores and into the output
  * rescaling; the probabilities are rounded to e4m3 for the second product
- * while the row normaliser is summed from the fp32 values.
+ * while the row normaliser is summed from the fp32 values.  The result is
+ * exact attention on the dequantised operands up to that rounding of the
+ * probabilities (at most 2^-4 relative per probability) and fp32 rounding.
  */
 int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
                const float* q_scale, const float* k_scale,
@@ -124,17 +135,27 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
                int d, float scale, int causal, void* stream);
 
 /*
- * fa_bwd -- attention backward by recomputation.
+ * fa_bwd -- attention backward by recomputation.  FlashAttention trains
+ * Transformers ("FlashAttention: Fast and Memory-Efficient Exact Attention
+ * with IO-Awareness", abstract), so the exact attention above needs its
+ * gradient; the abstract does not spell the backward out.  This computes the gradient of <dO, O> for O of fa_fwd, rebuilding
+ * the probabilities tile by tile from Q, K and the saved LSE so that the
+ * N x N matrix again never reaches HBM.
  *   q, k, v, o, dout : [B][H][N][d] of `dtype`, read only; o is the forward
  *                      output and lse the forward's log-sum-exp [B][H][N].
  *   dq               : [B][H][N][d] float, written (fp32 accumulation).
  *   dk, dv           : [B][H][N][d] of `dtype`, written.
  *   workspace        : device memory of at least
- *                      fa_bwd_workspace_size(B, H, N, d) bytes; its contents
- *                      on entry are ignored and on exit unspecified.
- * Gradients of <dO, O>: with P the probabilities rebuilt from Q, K and LSE,
- * D = rowsum(dO o O), dS = P o (dO V^T - D), the outputs are dV = P^T dO,
- * dK = scale dS^T Q and dQ = scale dS K.
+ *                      fa_bwd_workspace_size(B, H, N, d) bytes, 16-byte
+ *                      aligned; its contents on entry are ignored and on
+ *                      exit unspecified.
+ *   d                : 64 or 128 (d = 256 returns FA_ERR_UNSUPPORTED, and
+ *                      fa_bwd_workspace_size returns 0 for it).
+ *   Other arguments and errors as in fa_fwd.
+ * With P the probabilities rebuilt from Q, K and LSE, D = rowsum(dO o O),
+ * dS = P o (dO V^T - D), the outputs are dV = P^T dO, dK = scale dS^T Q and
+ * dQ = scale dS K.  dQ, dK and dV are deterministic: every element is
+ * written once, by one workgroup, with no atomics.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -149,11 +170,12 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  *     L = ln sum_p exp(L_p),    O = sum_p exp(L_p - L) O_p,
  * where O_p is the row's attention output over part p alone (normalised
  * over that part) and L_p its log-sum-exp (-inf when no key of the part is
- * visible; O_p is then 0).  This is the online softmax's rescaling applied
- * across parts ("FlashAttention-3: Fast and Accurate Attention with
- * Asynchrony and Low-precision", online-softmax description; Ring Attention
- * and Lean Attention in its reference list combine per-device and
- * per-split partials this way).
+ * visible; O_p is then 0).  This is the online softmax's rescaling (a
+ * running maximum and normaliser; FlashAttention-4 related-papers page,
+ * online-softmax snippet) applied across parts; Ring Attention and Lean
+ * Attention, in the reference list of "FlashAttention-3: Fast and Accurate
+ * Attention with Asynchrony and Low-precision", combine per-device and
+ * per-split partials this way.
  *
  * Positions.  With causal = 1, query row i of q sits at global position
  * q_pos0 + i, key row j of k at k_pos0 + j, and the key is visible iff its

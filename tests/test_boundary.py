@@ -119,6 +119,33 @@ def test_bwd_rejects_and_workspace(fa):
         assert fa.fa_bwd(**a) == code, kw
 
 
+def test_bwd_refuses_d256(fa):
+    """The backward is built for d = 64 and 128: d = 256 is refused before
+    anything is enqueued, and its workspace size is 0 (as include/fa.h
+    documents)."""
+    assert fa.fa_bwd_workspace_size(1, 1, 256, 256) == 0
+    assert fa.fa_bwd_workspace_size(1, 1, 256, 128) > 0
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE,
+                dv=FAKE, ws=FAKE, B=1, H=1, N=256, d=256, dtype=0, scale=0.0625, causal=0,
+                stream=None)
+    assert fa.fa_bwd(**args) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_internal_per_tile_hook_validates_like_fwd(fa):
+    """The per-tile schedule hook (exported, not in the header) shares
+    fa_fwd's argument checks."""
+    lib = fa.lib()
+    assert hasattr(lib, "fa_testing_fwd_per_tile")
+    assert "fa_testing_fwd_per_tile" not in _declared()
+    base = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=16, d=64,
+                dtype=fa.FA_BF16, scale=0.125, causal=1, stream=None)
+    for kw, code in ((dict(q=None), -1), (dict(N=0), -1), (dict(d=96), -2),
+                     (dict(scale=0.0), -1), (dict(causal=3), -1)):
+        a = dict(base)
+        a.update(kw)
+        assert fa.fa_testing_fwd_per_tile(**a) == code, kw
+
+
 def test_splitkv_entry_points_reject(fa):
     base = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, Nq=4, Nk=100, d=128,
                 dtype=0, scale=0.1, causal=1, q_pos0=96, k_pos0=0, stream=None)

@@ -202,9 +202,9 @@ def test_two_streams_concurrently():
                                      (3, 7, 4096, 128),    # 21 heads: unpinned, 2 rounds
                                      (1, 5, 3000, 64),     # ragged, one partial round
                                      (2, 9, 2048, 256)])   # 128-row tiles, 18 heads
-def test_causal_schedules_agree(B, H, N, d, monkeypatch):
+def test_causal_schedules_agree(B, H, N, d):
     """The persistent heaviest-first causal schedule (the default) and one
-    workgroup per query tile (FA_FWD_SCHED=1) run the same per-tile
+    workgroup per query tile (fa_testing_fwd_per_tile) run the same per-tile
     arithmetic, so they must agree bit for bit; every output element must be
     written (outputs start as NaN); sampled rows of the first and last heads
     match the oracle."""
@@ -214,11 +214,10 @@ def test_causal_schedules_agree(B, H, N, d, monkeypatch):
     (qt, kt, vt), (q64, k64, v64) = _case(B, H, N, d, 60 + d, "bf16")
     q, k, v = to_device(qt), to_device(kt), to_device(vt)
     res = []
-    for sched in ("0", "1"):
-        monkeypatch.setenv("FA_FWD_SCHED", sched)
+    for sched in (False, True):
         o = torch.full((B, H, N, d), float("nan"), dtype=torch.bfloat16, device="cuda")
         lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
-        fa.fwd(q, k, v, causal=True, out=o, lse=lse)
+        fa.fwd(q, k, v, causal=True, out=o, lse=lse, per_tile=sched)
         torch.cuda.synchronize()
         assert not torch.isnan(o).any() and not torch.isnan(lse).any(), sched
         res.append((o, lse))
