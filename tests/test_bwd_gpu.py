@@ -1,12 +1,19 @@
 """Backward parity: fa_bwd (HIP, through the C ABI) against the fp64 oracle.
 
 The device consumes its own forward output O and LSE (as a training step
-would); the oracle recomputes everything from the rounded Q, K, V, dO.  Bar,
-per gradient tensor: relative Frobenius error <= 1e-2 and max-abs error
-<= 5e-2 (no tolerance is stated for the backward; these follow from bf16
-rounding of P, dS and the outputs, a few 2^-9 relative each).  Full-size
-cases (B=4, H=16, N=4096, d=128, causal) are compared on whole heads that the
-oracle recomputes one at a time.
+would); the oracle recomputes everything from the rounded Q, K, V, dO.  No
+tolerance is stated for the backward; the bar is derived from its arithmetic.
+Rounding P and dS to bf16 before the matrix products and dK, dV to bf16 at
+the end (an fp64 emulation of exactly those roundings, one whole head of the
+B=4, H=16, N=4096, d=128 workload) gives relative Frobenius errors of
+2.4e-3 (dQ), 2.9e-3 (dK), 2.3e-3 (dV), which the device reproduces (1.7-1.9e-3,
+2.9-3.1e-3, 2.3e-3: dQ is stored in fp32).  Bar, per gradient tensor:
+  * relative Frobenius error <= 5e-3 (floor 1e-4 RMS for dQ == 0 cases);
+  * elementwise max-abs error <= 2^-7 max|ref| + 1e-4: one bf16 unit in the
+    last place at the tensor's largest magnitude (the emulated errors reach
+    26-52 % of it at every size tried).
+Full-size cases (B=4, H=16, N=4096, d=128) are compared on whole heads that
+the oracle recomputes one at a time.
 """
 
 import numpy as np
@@ -18,8 +25,9 @@ from tests.helpers import host_round, max_abs, to_device
 
 pytestmark = pytest.mark.gpu
 
-REL_FRO = 1e-2
-MAX_ABS = 5e-2
+REL_FRO = 5e-3
+MAX_ABS_REL = 2.0 ** -7   # of the largest reference magnitude
+MAX_ABS_FLOOR = 1e-4
 
 
 def _fa():
@@ -52,10 +60,12 @@ def _compare(got, ref, label):
         floor = 1e-4 * np.sqrt(r.size) / REL_FRO
         rel = np.linalg.norm(g - r) / max(np.linalg.norm(r), floor)
         ma = max_abs(g, r)
-        print(f"  {label} {name}: rel_fro={rel:.2e} max_abs={ma:.2e}")
-        assert rel <= REL_FRO, (label, name, rel)
-        assert ma <= MAX_ABS, (label, name, ma)
+        bar = MAX_ABS_REL * float(np.max(np.abs(r))) + MAX_ABS_FLOOR
+        print(f"  {label} {name}: rel_fro={rel:.2e} max_abs={ma:.2e} "
+              f"(bar {bar:.2e}, {ma / bar:.2f} of it)")
         assert np.all(np.isfinite(g))
+        assert rel <= REL_FRO, (label, name, rel)
+        assert ma <= bar, (label, name, ma, bar)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -99,7 +109,8 @@ def test_gradient_identities_on_device_output():
 
 
 def test_backward_repeatable():
-    """Repeated calls agree to fp32 atomic-reordering noise and dK/dV exactly."""
+    """Repeated calls agree bit for bit: every dQ, dK and dV element is
+    written once by one workgroup, with no atomics."""
     import torch
     fa = _fa()
     _banner("repeat")
@@ -113,5 +124,5 @@ def test_backward_repeatable():
     for _ in range(3):
         r = fa.bwd(qd, kd, vd, o, lse, dod, causal=True)
         torch.cuda.synchronize()
+        assert torch.equal(r[0], r0[0]), "dQ differs between calls"
         assert torch.equal(r[1], r0[1]) and torch.equal(r[2], r0[2])
-        assert torch.allclose(r[0], r0[0], rtol=1e-5, atol=1e-6)

@@ -4,9 +4,12 @@
   oracle's fp32 emulation (same butterfly order, fp32 division, RNE e4m3).
 * fa_fwd_fp8 runs on codes and scales produced by the *oracle's* quantiser and
   is compared with exact fp64 attention on the dequantised operands.  The
-  device additionally rounds the probabilities to e4m3, so the bar is the
-  elementwise worst-case bound of that rounding and twice its expected RMS
-  (oracle.fp8.p_rounding_bound / p_rounding_rms); LSE max-abs <= 1e-3.
+  device additionally rounds the probabilities to e4m3.  The gate is the RMS
+  of the error: at most twice the expected RMS of that rounding
+  (oracle.fp8.p_rounding_rms, plus the bf16 output rounding).  The
+  elementwise worst-case bound (oracle.fp8.p_rounding_bound) is checked too,
+  but at long sequences it exceeds a typical |O| and discriminates little;
+  LSE max-abs <= 1e-3.
 * On the outlier-injected workload (B=4, H=16, N=4096, d=128, 0.1 % of
   entries ~ N(0, 10^2)) the block-scaled + rotated path must have a lower
   RMSE than the per-tensor-scaled baseline, both measured end to end on the
@@ -128,22 +131,44 @@ def test_fwd_fp8_against_dequantised_oracle(d, N, causal):
     assert max_abs(lse, lse_ref) <= 1e-3
 
 
-def test_fwd_fp8_full_size_sampled_heads():
-    """B=4, H=16, N=4096, d=128 non-causal: whole heads against the oracle."""
-    _banner("fwd_fp8 full size")
+def _check_fp8_heads(ops, o, lse, heads, causal, label):
+    """Whole heads of a device result against the oracle on the same codes:
+    the RMS gate, the elementwise worst-case bound and the LSE."""
+    for b, h in heads:
+        sub = tuple(x[b:b + 1, h:h + 1] for x in ops)
+        o_ref, lse_ref = attention_fwd_fp8(*sub, causal=causal)
+        q, k, v = (dequantize_fp8(sub[i], sub[3 + i]) for i in range(3))
+        rms_expected = (p_rounding_rms(q, k, v, causal=causal)
+                        + 2.0 ** -9 * np.sqrt(np.mean(o_ref ** 2)))
+        got = o[b:b + 1, h:h + 1]
+        e = rmse(got, o_ref)
+        print(f"  {label} head ({b},{h}): rmse={e:.3e} (RMS gate {2 * rms_expected:.3e}) "
+              f"lse_max={max_abs(lse[b:b + 1, h:h + 1], lse_ref):.2e}")
+        assert e <= 2 * rms_expected, ("RMS gate", b, h, e, rms_expected)
+        assert np.all(np.abs(got - o_ref) <= p_rounding_bound(q, k, v, causal=causal)), (b, h)
+        assert max_abs(lse[b:b + 1, h:h + 1], lse_ref) <= 1e-3, (b, h)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_fp8_full_size_sampled_heads(causal):
+    """The fp8 workload, B=4, H=16, N=4096, d=128 (outlier inputs), causal
+    and not: whole heads against the oracle."""
+    _banner(f"fwd_fp8 full size causal={causal}")
     B, H, N, d = 4, 16, 4096, 128
     ops = _oracle_operands(B, H, N, d, 4)
-    o, lse = _dev_fwd_fp8(ops, False)
-    for b, h in ((0, 0), (2, 9), (3, 15)):
-        sub = tuple(x[b:b + 1, h:h + 1] for x in ops)
-        o_ref, lse_ref = attention_fwd_fp8(*sub)
-        q, k, v = (dequantize_fp8(sub[i], sub[3 + i]) for i in range(3))
-        bound = p_rounding_bound(q, k, v)
-        rms_bound = p_rounding_rms(q, k, v) + 2.0 ** -9 * np.sqrt(np.mean(o_ref ** 2))
-        got = o[b:b + 1, h:h + 1]
-        assert np.all(np.abs(got - o_ref) <= bound), (b, h)
-        assert rmse(got, o_ref) <= 2 * rms_bound, (b, h)
-        assert max_abs(lse[b:b + 1, h:h + 1], lse_ref) <= 1e-3
+    o, lse = _dev_fwd_fp8(ops, causal)
+    _check_fp8_heads(ops, o, lse, ((0, 0), (2, 9), (3, 15)), causal, "B=4 N=4096")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_fp8_bench_shape_sampled_heads(causal):
+    """B=2, H=16, N=8192, d=128 (the shape the benchmark times), outlier
+    inputs, causal and not: two whole heads against the oracle."""
+    _banner(f"fwd_fp8 B=2 N=8192 causal={causal}")
+    B, H, N, d = 2, 16, 8192, 128
+    ops = _oracle_operands(B, H, N, d, 4)
+    o, lse = _dev_fwd_fp8(ops, causal)
+    _check_fp8_heads(ops, o, lse, ((0, 3), (1, 14)), causal, "B=2 N=8192")
 
 
 def test_fp8_error_lower_than_per_tensor_baseline():

@@ -230,3 +230,71 @@ def test_probability_rounding_bounds_hold_for_simulated_rounding(causal):
     rms = np.sqrt(np.mean((sim - exact) ** 2))
     assert rms <= p_rounding_rms(q, k, v, causal=causal, scale=scale)
     assert rms > 0
+
+
+def _lagging_reference_attention(q, k, v, scale, causal, tile=64, bound=448.0):
+    """Online softmax whose exp reference lags the running maximum: the
+    reference is set on a row's first visible tile and raised to the running
+    maximum only when the tile's sum of exp(s - reference) exceeds `bound`,
+    so rounded values P~ = exp(s - reference) reach up to `bound` (the e4m3
+    maximum at 448).  P~ is rounded to e4m3 for the product with V; the
+    normaliser is summed from the unrounded values.  Returns O and the
+    largest P~ that was rounded."""
+    N = q.shape[0]
+    o = np.zeros_like(q)
+    p_max = 0.0
+    for i in range(N):
+        ref = -np.inf
+        acc = np.zeros(v.shape[1])
+        l = 0.0
+        for t0 in range(0, N, tile):
+            kk = np.arange(t0, min(t0 + tile, N))
+            if causal:
+                kk = kk[kk <= i]
+            if kk.size == 0:
+                continue
+            s = (k[kk] @ q[i]) * scale
+            if ref == -np.inf:
+                ref = s.max()
+            pt = np.exp(s - ref)
+            if pt.sum() > bound:
+                new = max(ref, s.max())
+                alpha = np.exp(ref - new)
+                acc *= alpha
+                l *= alpha
+                ref = new
+                pt = np.exp(s - ref)
+            p_max = max(p_max, float(pt.max()))
+            acc += e4m3_decode(e4m3_encode(pt)) @ v[kk]
+            l += pt.sum()
+        o[i] = acc / l
+    return o, p_max
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rounding_bounds_hold_for_lagging_reference(causal):
+    """The bounds of p_rounding_bound / p_rounding_rms are stated for any exp
+    reference at or below the row maximum.  Keys whose scores grow along the
+    sequence keep raising the running maximum, so a reference that is raised
+    only when a tile's sum passes 448 lags behind it and the rounded
+    probabilities exceed 1 (up to 448); both bounds must still hold."""
+    from oracle.fp8 import p_rounding_bound, p_rounding_rms
+    rng = np.random.default_rng(13)
+    B, H, N, d = 1, 1, 640, 64
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, d))
+    # Align the keys with the query mean and let their norm grow with the
+    # position: later keys score higher for most queries.
+    qbar = q[0, 0].mean(axis=0)
+    qbar /= np.linalg.norm(qbar)
+    k[0, 0] += np.outer(np.linspace(0.0, 12.0, N), qbar)
+    scale = 1.0 / 8.0
+    exact, _ = attention_fwd(q, k, v, causal=causal, scale=scale)
+    sim, p_max = _lagging_reference_attention(q[0, 0], k[0, 0], v[0, 0], scale, causal)
+    assert p_max > 16.0  # the reference really lagged the maximum
+    assert p_max <= 448.0
+    err = np.abs(sim - exact[0, 0])
+    assert np.all(err <= p_rounding_bound(q, k, v, causal=causal, scale=scale)[0, 0])
+    rms = np.sqrt(np.mean(err ** 2))
+    assert 0 < rms <= p_rounding_rms(q, k, v, causal=causal, scale=scale)
