@@ -68,6 +68,7 @@ __all__ = [
     "attention_fwd_online",
     "attention_fwd_rows",
     "default_scale",
+    "grad_rounding_bound",
 ]
 
 
@@ -370,3 +371,79 @@ def attention_fwd_blockmask(q, k, v, block_mask, block: int = 128,
             o[b, h][empty] = 0.0
             lse[b, h] = np.where(empty, -np.inf, m_safe + np.log(l_safe))
     return o, lse
+
+
+def grad_rounding_bound(q, k, v, do, causal: bool = False,
+                        scale: float | None = None, dtype: str = "bf16"):
+    """Elementwise bound on |gradient_device - gradient_exact| for a backward
+    by recomputation that rounds as follows (the device's arithmetic; the
+    pages do not describe the backward, so this is the reading it is held
+    to): scores, the log-sum-exp, D and all products accumulate in fp32 over
+    inputs of the 16-bit type; the rebuilt probabilities P and the products
+    dS = P o (dP - D) are rounded to the 16-bit type before they enter
+    matrix products; D is formed from the forward's stored O (itself the
+    result of a forward that rounds P and O to the 16-bit type); dK and dV
+    are rounded to the 16-bit type at the end, dQ stays fp32.
+
+    Rounding x to the 16-bit type errs by at most u |x| + eta: u = 2^-8
+    (bf16) or 2^-11 (fp16) for normal values, and eta = half the smallest
+    subnormal, 2^-134 (bf16) or 2^-25 (fp16), where the value falls into the
+    subnormal range or flushes to zero (small probabilities in fp16 do).
+
+    Arguments as for ``attention_bwd`` (the 16-bit values, widened).
+    Returns (bound_dQ, bound_dK, bound_dV), each [B,H,N,d] fp64.  First-order
+    worst case: every rounding error takes its largest magnitude and the
+    same sign, so at long sequences the bound is far above the typical
+    error (the relative Frobenius error is the sharper test).  A sum of n
+    fp32 terms is charged n 2^-24 times the sum of their magnitudes.
+    """
+    u, eta = {"bf16": (2.0 ** -8, 2.0 ** -134), "fp16": (2.0 ** -11, 2.0 ** -25)}[dtype]
+    return _grad_rounding_bound(q, k, v, do, causal, scale, u, eta)
+
+
+def _grad_rounding_bound(q, k, v, do, causal, scale, u, eta):
+    """grad_rounding_bound with the rounding constants given: relative
+    error u for normal values, absolute error eta where values underflow."""
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = default_scale(d)
+    f32 = 2.0 ** -24
+    g_d = d * f32          # sums over the head dimension
+    g_n = (N + 2) * f32    # sums over queries or keys
+    bq, bk, bv = (np.zeros_like(x) for x in (q, k, v))
+    for b in range(B):
+        for h in range(H):
+            Q, K, V, dO = q[b, h], k[b, h], v[b, h], do[b, h]
+            s = _scores(Q, K, scale, 0, causal)
+            p, _, _ = _softmax_rows(s)
+            vis = np.isfinite(s)
+            o = p @ V
+            # Absolute error of the rounded probability: fp32 scores and
+            # log-sum-exp (a relative error), then the rounding.
+            e_s = g_d * scale * (np.abs(Q) @ np.abs(K).T)
+            e_lse = g_n + np.max(np.where(vis, e_s, 0.0), axis=1, keepdims=True)
+            a = np.expm1(e_s + e_lse)
+            e_p = np.where(vis, (a + u + a * u) * p + eta, 0.0)
+            # The forward's stored O: rounded P, fp32 sums, O rounded.
+            e_o = (np.where(vis, u * p + eta, 0.0) + g_n * p) @ np.abs(V) \
+                + u * np.abs(o) + eta
+            dd = (dO * o).sum(axis=1, keepdims=True)
+            e_dd = (np.abs(dO) * e_o).sum(axis=1, keepdims=True) \
+                + g_d * (np.abs(dO) * np.abs(o)).sum(axis=1, keepdims=True)
+            dp = dO @ V.T
+            e_dp = g_d * (np.abs(dO) @ np.abs(V).T)
+            ds = p * (dp - dd)
+            e_ds = e_p * np.abs(dp - dd) + (p + e_p) * (e_dd + e_dp)
+            e_ds = np.where(vis, e_ds + u * (np.abs(ds) + e_ds) + eta, 0.0)  # dS rounded
+            ads = np.abs(ds) + e_ds
+            dv = p.T @ dO
+            ev = e_p.T @ np.abs(dO) + g_n * (p + e_p).T @ np.abs(dO)
+            bv[b, h] = ev + u * (np.abs(dv) + ev) + eta
+            dk = scale * (ds.T @ Q)
+            ek = scale * (e_ds.T @ np.abs(Q)) + g_n * scale * (ads.T @ np.abs(Q))
+            bk[b, h] = ek + u * (np.abs(dk) + ek) + eta
+            dq = scale * (ds @ K)
+            eq = scale * (e_ds @ np.abs(K)) + g_n * scale * (ads @ np.abs(K))
+            bq[b, h] = eq + 2 * f32 * (np.abs(dq) + eq)
+    return bq, bk, bv

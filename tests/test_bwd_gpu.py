@@ -2,16 +2,16 @@
 
 The device consumes its own forward output O and LSE (as a training step
 would); the oracle recomputes everything from the rounded Q, K, V, dO.  No
-tolerance is stated for the backward; the bar is derived from its arithmetic.
-Rounding P and dS to bf16 before the matrix products and dK, dV to bf16 at
-the end (an fp64 emulation of exactly those roundings, one whole head of the
-B=4, H=16, N=4096, d=128 workload) gives relative Frobenius errors of
-2.4e-3 (dQ), 2.9e-3 (dK), 2.3e-3 (dV), which the device reproduces (1.7-1.9e-3,
-2.9-3.1e-3, 2.3e-3: dQ is stored in fp32).  Bar, per gradient tensor:
-  * relative Frobenius error <= 5e-3 (floor 1e-4 RMS for dQ == 0 cases);
-  * elementwise max-abs error <= 2^-7 max|ref| + 1e-4: one bf16 unit in the
-    last place at the tensor's largest magnitude (the emulated errors reach
-    26-52 % of it at every size tried).
+tolerance is stated for the backward; the bar is derived from its arithmetic
+(P and dS rounded to the input type before the matrix products, D from the
+forward's rounded O, fp32 sums, dK and dV rounded at the end):
+  * relative Frobenius error per gradient <= 5e-3 for bf16, 1e-3 for fp16
+    (floor 1e-4 RMS for dQ == 0 cases).  A literal fp32/bf16 simulation of
+    that rounding model gives 2.2-3.5e-3 (bf16) and 2.9-4.1e-4 (fp16) on the
+    shapes below; the device reproduces it (dK 3.40e-3 at N=17, d=64 on both);
+  * every element within the worst-case bound of that rounding model
+    (oracle.attention.grad_rounding_bound; the simulation reaches at most
+    0.89 of it).
 Full-size cases (B=4, H=16, N=4096, d=128) are compared on whole heads that
 the oracle recomputes one at a time.
 """
@@ -20,14 +20,12 @@ import numpy as np
 import pytest
 
 from exact_tiled_attention_16_amd import inputs
-from oracle.attention import attention_bwd
+from oracle.attention import attention_bwd, grad_rounding_bound
 from tests.helpers import host_round, max_abs, to_device
 
 pytestmark = pytest.mark.gpu
 
-REL_FRO = 5e-3
-MAX_ABS_REL = 2.0 ** -7   # of the largest reference magnitude
-MAX_ABS_FLOOR = 1e-4
+REL_FRO = {"bf16": 5e-3, "fp16": 1e-3}
 
 
 def _fa():
@@ -53,19 +51,28 @@ def _grads(B, H, N, d, workload, causal, dtype="bf16", scale=None):
     return got, (q64, k64, v64, do64)
 
 
-def _compare(got, ref, label):
+def _check(got, inputs64, label, causal, dtype="bf16", scale=None, sl=None):
+    """Compare the device gradients (optionally the slice sl of them) with the
+    oracle on the matching inputs."""
+    q, k, v, do = (x if sl is None else x[sl] for x in inputs64)
+    ref = attention_bwd(q, k, v, do, causal=causal, scale=scale)
+    bound = grad_rounding_bound(q, k, v, do, causal=causal, scale=scale, dtype=dtype)
+    _compare(tuple(g if sl is None else g[sl] for g in got), ref, bound, label, dtype)
+
+
+def _compare(got, ref, bound, label, dtype):
     # The relative error has an absolute floor of 1e-4 RMS: when every query
     # sees a single key, dQ is exactly zero and only rounding noise remains.
-    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
-        floor = 1e-4 * np.sqrt(r.size) / REL_FRO
+    bar = REL_FRO[dtype]
+    for name, g, r, bd in zip(("dq", "dk", "dv"), got, ref, bound):
+        floor = 1e-4 * np.sqrt(r.size) / bar
         rel = np.linalg.norm(g - r) / max(np.linalg.norm(r), floor)
-        ma = max_abs(g, r)
-        bar = MAX_ABS_REL * float(np.max(np.abs(r))) + MAX_ABS_FLOOR
-        print(f"  {label} {name}: rel_fro={rel:.2e} max_abs={ma:.2e} "
-              f"(bar {bar:.2e}, {ma / bar:.2f} of it)")
+        err = np.abs(g - r)
+        print(f"  {label} {name}: rel_fro={rel:.2e} (bar {bar:.0e}) max_abs={err.max():.2e} "
+              f"max err/bound={float(np.max(err / bd)):.2f}")
         assert np.all(np.isfinite(g))
-        assert rel <= REL_FRO, (label, name, rel)
-        assert ma <= bar, (label, name, ma, bar)
+        assert rel <= bar, (label, name, rel)
+        assert np.all(err <= bd), (label, name, "elementwise rounding bound")
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -73,18 +80,16 @@ def _compare(got, ref, label):
 @pytest.mark.parametrize("causal", [False, True])
 def test_small_and_ragged(d, N, causal):
     _banner(f"d={d} N={N} causal={causal}")
-    got, (q, k, v, do) = _grads(2, 2, N, d, 500 + N + d, causal)
-    ref = attention_bwd(q, k, v, do, causal=causal)
-    _compare(got, ref, f"N={N}")
+    got, inp = _grads(2, 2, N, d, 500 + N + d, causal)
+    _check(got, inp, f"N={N}", causal)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 def test_dtypes_and_scale(dtype):
     _banner(f"dtype={dtype} scale=0.2")
     for causal in (False, True):
-        got, (q, k, v, do) = _grads(1, 2, 256, 128, 41, causal, dtype=dtype, scale=0.2)
-        ref = attention_bwd(q, k, v, do, causal=causal, scale=0.2)
-        _compare(got, ref, f"{dtype} causal={causal}")
+        got, inp = _grads(1, 2, 256, 128, 41, causal, dtype=dtype, scale=0.2)
+        _check(got, inp, f"{dtype} causal={causal}", causal, dtype=dtype, scale=0.2)
 
 
 @pytest.mark.parametrize("causal", [True, False])
@@ -92,11 +97,9 @@ def test_full_size_backward_heads(causal):
     """B=4, H=16, N=4096, d=128: three whole heads against the oracle."""
     _banner(f"full size causal={causal}")
     B, H, N, d = 4, 16, 4096, 128
-    got, (q, k, v, do) = _grads(B, H, N, d, 5, causal)
+    got, inp = _grads(B, H, N, d, 5, causal)
     for b, h in ((0, 0), (1, 7), (3, 15)):
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        ref = attention_bwd(q[sl], k[sl], v[sl], do[sl], causal=causal)
-        _compare(tuple(g[sl] for g in got), ref, f"head ({b},{h})")
+        _check(got, inp, f"head ({b},{h})", causal, sl=(slice(b, b + 1), slice(h, h + 1)))
 
 
 def test_gradient_identities_on_device_output():

@@ -267,3 +267,80 @@ def test_backward_row_block_independent():
     b = attention_bwd(q, k, v, do, causal=True, row_block=1024)
     for x, y in zip(a, b):
         assert np.max(np.abs(x - y)) <= 1e-13
+
+
+# ---------------------------------------------------------------- backward rounding bound
+
+def _round16(x, dtype):
+    import torch
+    t = {"bf16": torch.bfloat16, "fp16": torch.float16}[dtype]
+    return torch.from_numpy(np.ascontiguousarray(x)).to(t).double().numpy()
+
+
+def _simulated_rounded_backward(q, k, v, do, causal, scale, dtype):
+    """The rounding model that grad_rounding_bound states, carried out
+    literally: fp32 arithmetic (numpy float32) with P, the forward's O, dS,
+    dK and dV rounded to the 16-bit type at the stated points."""
+    B, H, N, d = q.shape
+    out = [np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)]
+    f = np.float32
+    for b in range(B):
+        for h in range(H):
+            Q, K, V, dO = (x[b, h].astype(f) for x in (q, k, v, do))
+            s = (Q @ K.T) * f(scale)
+            if causal:
+                s = np.where(np.arange(N)[None, :] > np.arange(N)[:, None], -np.inf, s).astype(f)
+            m = s.max(axis=1, keepdims=True)
+            e = np.exp(s - m).astype(f)
+            l = e.sum(axis=1, keepdims=True, dtype=f)
+            lse = (m + np.log(l)).astype(f)
+            o = _round16((_round16(e, dtype).astype(f) @ V) / l, dtype).astype(f)
+            p = _round16(np.exp(s - lse).astype(f), dtype).astype(f)
+            dd = (dO * o).sum(axis=1, keepdims=True, dtype=f)
+            ds = _round16(p * (dO @ V.T - dd), dtype).astype(f)
+            out[0][b, h] = (ds @ K) * f(scale)
+            out[1][b, h] = _round16(f(scale) * (ds.T @ Q), dtype)
+            out[2][b, h] = _round16(p.T @ dO, dtype)
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,scale", [(17, None), (129, None), (96, 0.2)])
+def test_grad_rounding_bound_holds_and_is_attained(dtype, causal, N, scale):
+    """The backward's elementwise rounding bound covers a literal simulation
+    of the rounding model it states (fp32 sums; P, O, dS, dK, dV rounded to
+    the 16-bit type, fp16 subnormals included), and is not vacuous: a
+    single-term gradient (dV of the last keys under the causal mask) comes
+    close to it."""
+    from oracle.attention import attention_bwd, grad_rounding_bound
+    rng = np.random.default_rng(21 + N)
+    B, H, d = 1, 2, 64
+    q, k, v, do = (_round16(rng.standard_normal((B, H, N, d)), dtype) for _ in range(4))
+    sc = scale if scale is not None else 1.0 / np.sqrt(d)
+    exact = attention_bwd(q, k, v, do, causal=causal, scale=sc)
+    sim = _simulated_rounded_backward(q, k, v, do, causal, sc, dtype)
+    bounds = grad_rounding_bound(q, k, v, do, causal=causal, scale=sc, dtype=dtype)
+    ratios = []
+    for g, r, bd in zip(sim, exact, bounds):
+        err = np.abs(g - r)
+        assert np.all(err <= bd)
+        ratios.append(float(np.max(err / bd)))
+    if causal and scale is None:
+        assert ratios[2] >= 0.5, ratios
+
+
+def test_grad_rounding_bound_needs_its_underflow_term():
+    """With fp16 and a small softmax scale many probabilities underflow; a
+    bound without the absolute subnormal term fails there (the relative
+    model alone is not enough), the stated one holds."""
+    from oracle.attention import _grad_rounding_bound, attention_bwd, grad_rounding_bound
+    rng = np.random.default_rng(5)
+    B, H, N, d = 1, 2, 256, 128
+    q, k, v, do = (_round16(rng.standard_normal((B, H, N, d)), "fp16") for _ in range(4))
+    exact = attention_bwd(q, k, v, do, causal=True, scale=0.2)
+    sim = _simulated_rounded_backward(q, k, v, do, True, 0.2, "fp16")
+    full = grad_rounding_bound(q, k, v, do, causal=True, scale=0.2, dtype="fp16")
+    rel_only = _grad_rounding_bound(q, k, v, do, True, 0.2, 2.0 ** -11, 0.0)
+    assert all(np.all(np.abs(g - r) <= b) for g, r, b in zip(sim, exact, full))
+    assert np.any(np.abs(sim[2] - exact[2]) > rel_only[2])
