@@ -37,6 +37,7 @@
 //                   tile) is bound by the L2 atomic units.
 //   Rows past N (queries or keys) arrive as zeros; every product they enter
 //   is then exactly zero or never stored, so only the causal mask is applied.
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -746,6 +747,48 @@ hipError_t launch_bwd(const BwdArgs& a, int B, int H, int d, int dtype, bool cau
   const int BH = B * H;
   return dtype == 0 ? launch_dtype<0>(a, BH, d, causal, stream)
                     : launch_dtype<1>(a, BH, d, causal, stream);
+}
+
+// ---------------------------------------------------------------- no-alloc
+
+// Fixed device scratch of the allocation-free backward (fa_bwd_noalloc): it
+// holds the two per-row planes that fa_bwd keeps in the caller's workspace.
+// Each device holds its own copy, at its own address, for the life of the
+// process.  In host code `scratch` names a host-side stand-in, never the
+// device memory: kernels and copies only ever get the address that
+// hipGetSymbolAddress returns for the current device (cached below).
+static __device__ __align__(256) uint8_t scratch[kBwdScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+
+// Device address of `scratch` on the current device, looked up on the first
+// call on that device; null if the lookup fails.
+void* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr)
+      return nullptr;
+    g_scratch_ptr[dev].store(q, std::memory_order_release);
+    p = q;
+  }
+  return p;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_noalloc(const BwdArgs& a0, int B, int H, int d, int dtype, bool causal,
+                              hipStream_t stream) {
+  void* p = scratch_on_current_device();
+  if (p == nullptr) return hipErrorInvalidSymbol;
+  BwdArgs a = a0;
+  a.dsum = static_cast<float*>(p);
+  return launch_bwd(a, B, H, d, dtype, causal, stream);
 }
 
 }  // namespace fa

@@ -39,6 +39,9 @@ const char* fa_status_str(int status) {
     case FA_ERR_INVALID: return "invalid argument (null or misaligned pointer, bad size, dtype or scale)";
     case FA_ERR_UNSUPPORTED: return "unsupported configuration (head dimension must be 64, 128 or 256)";
     case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_TOO_LARGE:
+      return "problem too large for the fixed scratch of fa_bwd_noalloc "
+             "(B*H*N above FA_BWD_NOALLOC_MAX_ROWS)";
     default: return "unknown status";
   }
 }
@@ -263,18 +266,26 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   return (size_t)B * H * N * 2 * sizeof(float);  // per row: LSE * log2 e, rowsum(dO o O)
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-           const float* lse, float* dq, void* dk, void* dv, void* workspace, int B, int H,
-           int N, int d, int dtype, float scale, int causal, void* stream) {
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
-    return FA_ERR_INVALID;
+namespace {
+
+// Argument checks shared by fa_bwd and fa_bwd_noalloc (everything but the
+// workspace pointer).
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+              const float* lse, float* dq, void* dk, void* dv, int B, int H, int N, int d,
+              int dtype, float scale, int causal) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
-      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) ||
-      !aligned4(lse))
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned4(lse))
     return FA_ERR_INVALID;
   if (!valid_dims(B, H, N) || (dtype != FA_BF16 && dtype != FA_FP16)) return FA_ERR_INVALID;
   if (!valid_scale(scale) || (causal != 0 && causal != 1)) return FA_ERR_INVALID;
   if (!supported_d(d) || !fa::bwd_supported(d)) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, float* dq, void* dk, void* dv,
+                     void* workspace, int N, float scale) {
   fa::BwdArgs a{};
   a.q = q;
   a.k = k;
@@ -289,9 +300,34 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   a.N = N;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
+  return a;
+}
+
+}  // namespace
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, float* dq, void* dk, void* dv, void* workspace, int B, int H,
+           int N, int d, int dtype, float scale, int causal, void* stream) {
+  if (!workspace || !aligned16(workspace)) return FA_ERR_INVALID;
+  const int rc = check_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, dtype, scale, causal);
+  if (rc != FA_OK) return rc;
+  const fa::BwdArgs a = bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, N, scale);
   return launch_status(
       fa::launch_bwd(a, B, H, d, dtype, causal != 0, static_cast<hipStream_t>(stream)));
 }
 
-}  // extern "C"
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, float* dq, void* dk, void* dv, int B, int H, int N, int d,
+                   int dtype, float scale, int causal, void* stream) {
+  const int rc = check_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, dtype, scale, causal);
+  if (rc != FA_OK) return rc;
+  static_assert((size_t)FA_BWD_NOALLOC_MAX_ROWS * 2 * sizeof(float) == fa::kBwdScratchBytes,
+                "scratch size and the documented row limit agree");
+  if ((int64_t)B * H * N > FA_BWD_NOALLOC_MAX_ROWS) return FA_ERR_TOO_LARGE;
+  if (fa_bwd_workspace_size(B, H, N, d) > fa::kBwdScratchBytes) return FA_ERR_TOO_LARGE;
+  const fa::BwdArgs a = bwd_args(q, k, v, o, dout, lse, dq, dk, dv, nullptr, N, scale);
+  return launch_status(
+      fa::launch_bwd_noalloc(a, B, H, d, dtype, causal != 0, static_cast<hipStream_t>(stream)));
+}
 
+}  // extern "C"

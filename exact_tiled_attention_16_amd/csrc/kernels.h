@@ -119,4 +119,13 @@ bool bwd_supported(int d);
 hipError_t launch_bwd(const BwdArgs& a, int B, int H, int d, int dtype, bool causal,
                       hipStream_t stream);
 
+// Size of the fixed device scratch of the allocation-free backward: the
+// backward's per-row workspace for up to kBwdScratchBytes / 8 rows (B*H*N).
+constexpr size_t kBwdScratchBytes = size_t(16) << 20;
+
+// launch_bwd with the workspace in the fixed device scratch (a.dsum is
+// ignored); the caller checks the size against kBwdScratchBytes.
+hipError_t launch_bwd_noalloc(const BwdArgs& a, int B, int H, int d, int dtype, bool causal,
+                              hipStream_t stream);
+
 }  // namespace fa

@@ -23,6 +23,8 @@ FA_OK = 0
 FA_ERR_INVALID = -1
 FA_ERR_UNSUPPORTED = -2
 FA_ERR_LAUNCH = -3
+FA_ERR_TOO_LARGE = -4
+BWD_NOALLOC_MAX_ROWS = 2097152
 FA_BF16 = 0
 FA_FP16 = 1
 FP8_BLOCK = 128
@@ -39,6 +41,8 @@ SIGNATURES = {
     "fa_bwd_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
                     _I, _F, _I, _P]),
+    "fa_bwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I,
+                            _I, _I, _F, _I, _P]),
     "fa_fwd_partial": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
                             _I, _I, _P]),
     "fa_merge": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _P]),
@@ -124,6 +128,12 @@ def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, B, H, N, d, dtype, scale,
            causal, stream) -> int:
     return lib().fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, B, H, N, d,
                         dtype, scale, causal, stream)
+
+
+def fa_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, B, H, N, d, dtype, scale,
+                   causal, stream) -> int:
+    return lib().fa_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, B, H, N, d,
+                                dtype, scale, causal, stream)
 
 
 def fa_fwd_partial(q, k, v, o, lse, B, H, Nq, Nk, d, dtype, scale, causal,

@@ -53,6 +53,7 @@ extern "C" {
 #define FA_ERR_INVALID (-1)
 #define FA_ERR_UNSUPPORTED (-2)
 #define FA_ERR_LAUNCH (-3)
+#define FA_ERR_TOO_LARGE (-4) /* above the fixed scratch of fa_bwd_noalloc */
 
 /* Element types of the 16-bit inputs. */
 #define FA_BF16 0
@@ -162,6 +163,32 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse, float* dq, void* dk, void* dv,
            void* workspace, int B, int H, int N, int d, int dtype, float scale,
            int causal, void* stream);
+
+/*
+ * fa_bwd_noalloc -- fa_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and outputs (bit for bit), with the
+ * workspace taken from a fixed scratch array in the library's device code
+ * instead of a caller buffer.  It calls no hipMalloc, hipFree or other
+ * allocating routine; on its first call on a device it looks up that
+ * device's copy of the array (hipGetSymbolAddress) and keeps the address.
+ *   Arguments : as in fa_bwd, without `workspace`.
+ *   Limit     : B * H * N <= FA_BWD_NOALLOC_MAX_ROWS (the scratch is
+ *               FA_BWD_NOALLOC_MAX_ROWS * 8 bytes = 16 MiB per device, held
+ *               until the process ends); larger problems return
+ *               FA_ERR_TOO_LARGE before anything is enqueued.
+ *   Errors    : as in fa_bwd; FA_ERR_LAUNCH also if the scratch cannot be
+ *               looked up on the current device.
+ * Every call on one device shares that device's scratch: calls that
+ * overlap in time on one device (different streams, or host threads) race
+ * and must be serialised by the caller.  Nothing in the scratch needs to
+ * start at zero (each call overwrites what it reads).
+ */
+#define FA_BWD_NOALLOC_MAX_ROWS 2097152
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, float* dq, void* dk,
+                   void* dv, int B, int H, int N, int d, int dtype,
+                   float scale, int causal, void* stream);
 
 /*
  * Split-KV attention: partial results over parts of the keys, and their

@@ -41,7 +41,7 @@ def fa():
 
 def test_header_declares_expected_entry_points():
     d = _declared()
-    assert {"fa_fwd", "fa_quant_fp8", "fa_fwd_fp8", "fa_bwd",
+    assert {"fa_fwd", "fa_quant_fp8", "fa_fwd_fp8", "fa_bwd", "fa_bwd_noalloc",
             "fa_bwd_workspace_size", "fa_status_str", "fa_fwd_partial", "fa_merge",
             "fa_splitkv_workspace_size", "fa_fwd_splitkv", "fa_fwd_blocksparse",
             "fa_blocksparse_workspace_size"} <= set(d)
@@ -56,7 +56,8 @@ def test_library_exports_every_declared_symbol(fa):
 
 
 def test_status_strings(fa):
-    for code in (fa.FA_OK, fa.FA_ERR_INVALID, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_LAUNCH):
+    for code in (fa.FA_OK, fa.FA_ERR_INVALID, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_LAUNCH,
+                 fa.FA_ERR_TOO_LARGE):
         assert fa.status_str(code) and fa.status_str(code) != "unknown status"
     assert fa.status_str(12345) == "unknown status"
 
@@ -216,3 +217,22 @@ def test_clock_probe_library_exports():
     lib.fa_probe_clock.restype = ctypes.c_int
     lib.fa_probe_clock.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p]
     assert lib.fa_probe_clock(None, 100, None) == -1  # rejected before any launch
+
+
+def test_bwd_noalloc_rejects(fa):
+    """The allocation-free backward checks its arguments like fa_bwd and
+    refuses problems beyond its fixed scratch, all before touching the
+    device."""
+    base = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE,
+                dv=FAKE, B=1, H=1, N=16, d=128, dtype=0, scale=0.1, causal=1, stream=None)
+    rows = fa.BWD_NOALLOC_MAX_ROWS
+    for kw, code in ((dict(do=None), -1), (dict(lse=None), -1), (dict(dq=FAKE + 4), -1),
+                     (dict(N=0), -1), (dict(dtype=7), -1), (dict(scale=0.0), -1),
+                     (dict(d=256), -2), (dict(d=80), -2),
+                     (dict(B=1, H=1, N=rows + 1), fa.FA_ERR_TOO_LARGE),
+                     (dict(B=16, H=32, N=4097), fa.FA_ERR_TOO_LARGE),
+                     (dict(B=rows, H=2, N=1), fa.FA_ERR_TOO_LARGE)):
+        a = dict(base)
+        a.update(kw)
+        assert fa.fa_bwd_noalloc(**a) == code, kw
+    assert "fa_bwd_noalloc" in fa.status_str(fa.FA_ERR_TOO_LARGE)
