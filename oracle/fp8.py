@@ -195,19 +195,43 @@ def attention_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale,
     return attention_fwd(q, k, v, causal=causal, scale=scale)
 
 
+def _e4m3_spacing(x):
+    """Distance between neighbouring e4m3 values around x >= 0: 2^(e-3) for
+    a normal value with binary exponent e >= -6, the subnormal spacing 2^-9
+    below 2^-6."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(x > 0, x, 1.0)))
+    return np.ldexp(1.0, (np.maximum(e, 1 - _BIAS) - 3).astype(np.int64))
+
+
+def _scores_probs(q, k, scale, causal):
+    """Scores of one head (masked), the unnormalised probabilities against
+    the row maximum (P~ <= 1) and their row sums."""
+    N = q.shape[0]
+    s = (q @ k.T) * scale
+    if causal:
+        s = np.where(np.arange(N)[None, :] > np.arange(N)[:, None], -np.inf, s)
+    m = s.max(axis=1, keepdims=True)
+    pt = np.exp(s - m)
+    return s, pt, pt.sum(axis=1, keepdims=True)
+
+
 def p_rounding_bound(q, k, v, causal: bool = False, scale: float | None = None):
     """Elementwise bound on |O_device - O_exact| for attention whose
     probabilities are rounded to e4m3 before the second product.
 
     Arguments are the dequantised operands (fp64 [B, H, N, d]).  The device
-    rounds P~ = exp(s - m_t) (m_t a running maximum, m_t <= the row maximum
-    m) to e4m3; the rounded value differs from P~ by at most 2^-4 P~ when P~
-    is normal (>= 2^-6) and by at most 2^-10 (half the subnormal spacing 2^-9)
-    below that.  After the rescaling to the final maximum the contribution of
-    key j to row i is therefore at most
-        max(2^-4 p_ij |v_j|, 2^-10 |v_j| / l_i),   l_i = sum_j exp(s_ij - m_i) >= 1,
-    so the bound is 2^-4 (P |V|)_i + 2^-10 (sum_j |v_j|) / l_i, plus 2^-8 |O|
-    for the bf16 output rounding and fp32 arithmetic.
+    rounds P~ = exp(s - r) with a reference r at or below the row maximum m
+    (so P~ is at least exp(s - m)) to e4m3.  Rounding to nearest errs by at
+    most half the spacing: 2^-4 P~ for a normal value (>= 2^-6), 2^-10 (half
+    the subnormal spacing 2^-9) below that, and P~ itself for a value that
+    rounds to zero.  Measured against the row maximum (multiply by
+    exp(r - m) <= 1 and divide by l = sum_j exp(s_j - m) >= 1) the error of
+    key j in row i is therefore at most
+        max(2^-4 p_ij, min(p_ij, 2^-10 / l_i)),    p = softmax probability,
+    whatever the reference, and the bound is the sum of that times |v_j|,
+    plus 2^-8 |O| for the bf16 output rounding and fp32 arithmetic.
     """
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     B, H, N, d = q.shape
@@ -216,27 +240,32 @@ def p_rounding_bound(q, k, v, causal: bool = False, scale: float | None = None):
     bound = np.empty_like(q)
     for b in range(B):
         for h in range(H):
-            s = (q[b, h] @ k[b, h].T) * scale
-            if causal:
-                s = np.where(np.arange(N)[None, :] > np.arange(N)[:, None], -np.inf, s)
-            m = s.max(axis=1, keepdims=True)
-            e = np.exp(s - m)
-            l = e.sum(axis=1, keepdims=True)
-            p = e / l
-            av = np.abs(v[b, h])
-            vis = np.isfinite(s).astype(np.float64)
+            _, pt, l = _scores_probs(q[b, h], k[b, h], scale, causal)
+            p = pt / l
+            e = np.maximum(2.0 ** -4 * p, np.minimum(p, 2.0 ** -10 / l))
             o = p @ v[b, h]
-            bound[b, h] = (2.0 ** -4) * (p @ av) + (2.0 ** -10) * (vis @ av) / l \
-                + (2.0 ** -8) * np.abs(o) + 1e-6
+            bound[b, h] = e @ np.abs(v[b, h]) + (2.0 ** -8) * np.abs(o) + 1e-6
     return bound
 
 
 def p_rounding_rms(q, k, v, causal: bool = False, scale: float | None = None):
     """Expected RMS of O_device - O_exact over all elements when the e4m3
-    rounding errors of different probabilities are independent and uniform:
-    each contributes at most (2^-4 p_ij)^2 / 3 (normal) or (2^-10 / l_i)^2 / 3
-    (subnormal) times v_jc^2 to the variance of element (i, c).  Arguments as
-    in ``p_rounding_bound``."""
+    rounding errors of different probabilities are independent and each is
+    uniform over the rounding interval of its value (variance spacing^2 / 12,
+    spacing from the e4m3 format), except that a value below half the
+    smallest subnormal (2^-10) rounds to zero with error equal to itself,
+    and a value on the e4m3 grid has no error.
+
+    Reading of the reference: the probabilities are taken against the row
+    maximum, so the maximum's own P~ = exp(0) = 1 is exact.  A reference
+    that lags the maximum scales every value alike: in the normal range
+    that leaves the relative error unchanged, values leave the subnormal
+    range (less error), and only the maximum itself loses its exactness.
+    The device raises its reference on the tile where a key dominating the
+    row arrives (the tile's sum then exceeds the bound of 448), which is
+    where that last term would be large; on flat rows p_max is small.  The
+    worst case over any reference is ``p_rounding_bound``.
+    Arguments as in ``p_rounding_bound``."""
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     B, H, N, d = q.shape
     if scale is None:
@@ -244,14 +273,8 @@ def p_rounding_rms(q, k, v, causal: bool = False, scale: float | None = None):
     total = 0.0
     for b in range(B):
         for h in range(H):
-            s = (q[b, h] @ k[b, h].T) * scale
-            if causal:
-                s = np.where(np.arange(N)[None, :] > np.arange(N)[:, None], -np.inf, s)
-            m = s.max(axis=1, keepdims=True)
-            e = np.exp(s - m)
-            l = e.sum(axis=1, keepdims=True)
-            p = e / l
-            w = np.maximum((2.0 ** -8) * p * p, (2.0 ** -20) / (l * l))
-            w = np.where(np.isfinite(s), w, 0.0)
-            total += float(np.sum(w @ (v[b, h] ** 2))) / 3.0
+            _, pt, l = _scores_probs(q[b, h], k[b, h], scale, causal)
+            var = np.where(pt < 2.0 ** -10, pt * pt, _e4m3_spacing(pt) ** 2 / 12.0)
+            var = np.where(pt == 1.0, 0.0, var)
+            total += float(np.sum((var / (l * l)) @ (v[b, h] ** 2)))
     return math.sqrt(total / q.size)

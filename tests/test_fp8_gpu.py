@@ -124,8 +124,9 @@ def test_fwd_fp8_against_dequantised_oracle(d, N, causal):
     bound = p_rounding_bound(q, k, v, causal=causal)
     rms_bound = p_rounding_rms(q, k, v, causal=causal) + 2.0 ** -9 * np.sqrt(np.mean(o_ref ** 2))
     err = np.abs(o - o_ref)
-    print(f"  rmse={rmse(o, o_ref):.3e} (2x expected {2 * rms_bound:.3e}) "
-          f"max={err.max():.3e} lse_max={max_abs(lse, lse_ref):.2e}")
+    print(f"  rmse={rmse(o, o_ref):.3e} (RMS gate {2 * rms_bound:.3e}, "
+          f"{rmse(o, o_ref) / (2 * rms_bound):.2f} of it) max err/bound="
+          f"{float(np.max(err / bound)):.2f} lse_max={max_abs(lse, lse_ref):.2e}")
     assert np.all(err <= bound)
     assert rmse(o, o_ref) <= 2 * rms_bound
     assert max_abs(lse, lse_ref) <= 1e-3
@@ -142,7 +143,8 @@ def _check_fp8_heads(ops, o, lse, heads, causal, label):
                         + 2.0 ** -9 * np.sqrt(np.mean(o_ref ** 2)))
         got = o[b:b + 1, h:h + 1]
         e = rmse(got, o_ref)
-        print(f"  {label} head ({b},{h}): rmse={e:.3e} (RMS gate {2 * rms_expected:.3e}) "
+        print(f"  {label} head ({b},{h}): rmse={e:.3e} (RMS gate {2 * rms_expected:.3e}, "
+              f"{e / (2 * rms_expected):.2f} of it) "
               f"lse_max={max_abs(lse[b:b + 1, h:h + 1], lse_ref):.2e}")
         assert e <= 2 * rms_expected, ("RMS gate", b, h, e, rms_expected)
         assert np.all(np.abs(got - o_ref) <= p_rounding_bound(q, k, v, causal=causal)), (b, h)

@@ -228,8 +228,11 @@ def test_probability_rounding_bounds_hold_for_simulated_rounding(causal):
     bound = p_rounding_bound(q, k, v, causal=causal, scale=scale)
     assert np.all(np.abs(sim - exact) <= bound)
     rms = np.sqrt(np.mean((sim - exact) ** 2))
-    assert rms <= p_rounding_rms(q, k, v, causal=causal, scale=scale)
-    assert rms > 0
+    # The expected RMS predicts the simulated one (an error in the e4m3
+    # spacing, the uniform variance or the flush-to-zero term moves the
+    # ratio by a factor of 1.5 or more).
+    ratio = rms / p_rounding_rms(q, k, v, causal=causal, scale=scale)
+    assert 0.8 <= ratio <= 1.25, ratio
 
 
 def _lagging_reference_attention(q, k, v, scale, causal, tile=64, bound=448.0):
@@ -296,5 +299,8 @@ def test_probability_rounding_bounds_hold_for_lagging_reference(causal):
     assert p_max <= 448.0
     err = np.abs(sim - exact[0, 0])
     assert np.all(err <= p_rounding_bound(q, k, v, causal=causal, scale=scale)[0, 0])
-    rms = np.sqrt(np.mean(err ** 2))
-    assert 0 < rms <= p_rounding_rms(q, k, v, causal=causal, scale=scale)
+    # A lagging reference also rounds the row maximum's own probability; the
+    # RMS stays within a small factor of the exact-reference expectation
+    # (the device's gate allows twice it).
+    ratio = np.sqrt(np.mean(err ** 2)) / p_rounding_rms(q, k, v, causal=causal, scale=scale)
+    assert 0.8 <= ratio <= 1.5, ratio
