@@ -37,6 +37,7 @@
 //                   tile) is bound by the L2 atomic units.
 //   Rows past N (queries or keys) arrive as zeros; every product they enter
 //   is then exactly zero or never stored, so only the causal mask is applied.
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 
@@ -126,7 +127,7 @@ __device__ __forceinline__ int swz(int r) {
 // buffers inside LDS next to three query-tile stages; dS' is formed from it
 // in fp32.  Tile i+1 is copied at the start of tile i into the stage of tile
 // i-2, free since the previous barrier.
-template <int D, int BQ, bool CAUSAL, int DT>
+template <int D, int BQ, bool CAUSAL, int DT, bool PERSIST>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_kv3_kernel(BwdArgs a) {
   using E = Elem<DT>;
@@ -151,17 +152,20 @@ bwd_kv3_kernel(BwdArgs a) {
   FA_LDS uint8_t* lds = (FA_LDS uint8_t*)smem;
   FA_LDS uint8_t* p_lds = lds + NSTG * STAGEB;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int kb = wave & 3;
-  const int hl = lane >> 5;
-  const int l32 = lane & 31;
   const int N = a.N;
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / a.n_ktiles;
-  const int kt = logical % a.n_ktiles;
+  // One work unit: key tile kt of head bh.
+  auto unit = [&](const int bh, const int kt) {
+  // The lane index passes through an empty asm so that nothing derived from
+  // it is hoisted out of a loop over units (it would stay live across units
+  // and spill at the register limit).
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int hl = lane >> 5;
+  const int l32 = lane & 31;
   const int64_t base = (int64_t)bh * N * D;
   const uint16_t* Qg = static_cast<const uint16_t*>(a.q) + base;
   const uint16_t* dOg = static_cast<const uint16_t*>(a.dout) + base;
@@ -421,6 +425,21 @@ bwd_kv3_kernel(BwdArgs a) {
     run(std::integral_constant<int, 0>{});
   else
     run(std::integral_constant<int, 1>{});
+  };  // unit
+
+  if constexpr (PERSIST) {
+    // Causal: key tile kt meets the query tiles from its diagonal on, so
+    // rank 0 (the heaviest) is key tile 0.
+    lpt_units(a.n_ktiles, a.bh, a.pin != 0, [&](int bh, int rank) {
+      unit(bh, rank);
+      // The next unit's first copies reuse the ring and the P buffers.
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    });
+  } else {
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    unit(logical / a.n_ktiles, logical % a.n_ktiles);
+  }
 }
 
 // dQ by recomputation, query-stationary: one workgroup per (b, h, tile of
@@ -437,7 +456,7 @@ bwd_kv3_kernel(BwdArgs a) {
 // K and V tiles stream through a four-stage ring filled by buffer loads with
 // an LDS destination, two tiles per workgroup barrier; two waves share each
 // SIMD, so one wave's vector work overlaps the other's matrix work.
-template <int D, int BN, int NW, bool CAUSAL, int DT>
+template <int D, int BN, int NW, bool CAUSAL, int DT, bool PERSIST>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dq_kernel(BwdArgs a) {
   using E = Elem<DT>;
@@ -460,17 +479,16 @@ bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NSTG * TILEB];
   FA_LDS uint8_t* lds = (FA_LDS uint8_t*)smem;  // K stage s at s*TILEB, V at (NSTG+s)*TILEB
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hl = lane >> 5;
-  const int l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int N = a.N;
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / a.n_ktiles;  // n_ktiles holds the query-tile count here
-  int qt = logical % a.n_ktiles;
-  if (CAUSAL) qt = a.n_ktiles - 1 - qt;  // longest key ranges first
+  // One work unit: query tile qt of head bh.
+  auto unit = [&](const int bh, const int qt) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));  // as in the dK/dV kernel: nothing hoisted
+  const int lane = tid & 63;
+  const int hl = lane >> 5;
+  const int l32 = lane & 31;
   const int64_t base = (int64_t)bh * N * D;
   const uint16_t* Qg = static_cast<const uint16_t*>(a.q) + base;
   const uint16_t* Kg = static_cast<const uint16_t*>(a.k) + base;
@@ -690,6 +708,44 @@ bwd_dq_kernel(BwdArgs a) {
             f32x4_t{dqacc[db][4 * g], dqacc[db][4 * g + 1], dqacc[db][4 * g + 2], dqacc[db][4 * g + 3]} *
             a.scale;
   }
+  };  // unit
+
+  // n_ktiles holds the query-tile count in this kernel.
+  if constexpr (PERSIST) {
+    // Causal: query tile qt meets the key tiles up to its diagonal, so rank
+    // 0 (the heaviest) is the last query tile.
+    lpt_units(a.n_ktiles, a.bh, a.pin != 0, [&](int bh, int rank) {
+      unit(bh, a.n_ktiles - 1 - rank);
+      // The next unit's first copies reuse the ring.
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    });
+  } else {
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    int qt = logical % a.n_ktiles;
+    if (CAUSAL) qt = a.n_ktiles - 1 - qt;  // longest key ranges first
+    unit(logical / a.n_ktiles, qt);
+  }
+}
+
+// Launches one of the two main kernels over a.n_ktiles tiles of each of BH
+// heads: non-causal, one workgroup per tile (all tiles cost the same);
+// causal, the persistent heaviest-first schedule with one workgroup per
+// resident slot.
+template <auto KPlain, auto KPersist>
+hipError_t launch_grid(BwdArgs a, int BH, bool causal, int threads, hipStream_t s) {
+  const int64_t units = (int64_t)a.n_ktiles * BH;
+  if (units > 0x7fffffff) return hipErrorInvalidValue;
+  if (!causal) {
+    hipLaunchKernelGGL(KPlain, dim3((unsigned)units), dim3(threads), 0, s, a);
+    return hipGetLastError();
+  }
+  const int slots = resident_slots(KPersist, threads);
+  if (slots <= 0) return hipErrorInvalidValue;
+  const int64_t grid = std::min<int64_t>(units, slots);
+  a.pin = (BH % 8 == 0 && grid % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL(KPersist, dim3((unsigned)grid), dim3(threads), 0, s, a);
+  return hipGetLastError();
 }
 
 template <int D, int NW, int BQ, int DQ_BN, int DQ_NW, int DT>
@@ -705,28 +761,17 @@ hipError_t launch_d(const BwdArgs& a0, int BH, bool causal, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   a.plane = rows;
+  a.bh = BH;
   constexpr int BKV = 128;
   a.n_ktiles = (a.N + BKV - 1) / BKV;
-  int64_t grid = (int64_t)a.n_ktiles * BH;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  if (causal)
-    hipLaunchKernelGGL((bwd_kv3_kernel<D, BQ, true, DT>), dim3((unsigned)grid), dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_kv3_kernel<D, BQ, false, DT>), dim3((unsigned)grid), dim3(512), 0, s, a);
-
-  e = hipGetLastError();
+  e = launch_grid<bwd_kv3_kernel<D, BQ, false, DT, false>, bwd_kv3_kernel<D, BQ, true, DT, true>>(
+      a, BH, causal, 512, s);
   if (e != hipSuccess) return e;
   constexpr int BM = 32 * DQ_NW;
   a.n_ktiles = (a.N + BM - 1) / BM;  // query tiles for the dQ kernel
-  grid = (int64_t)a.n_ktiles * BH;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  if (causal)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, DQ_BN, DQ_NW, true, DT>), dim3((unsigned)grid),
-                       dim3(DQ_NW * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, DQ_BN, DQ_NW, false, DT>), dim3((unsigned)grid),
-                       dim3(DQ_NW * 64), 0, s, a);
-  return hipGetLastError();
+  return launch_grid<bwd_dq_kernel<D, DQ_BN, DQ_NW, false, DT, false>,
+                     bwd_dq_kernel<D, DQ_BN, DQ_NW, true, DT, true>>(a, BH, causal, DQ_NW * 64,
+                                                                      s);
 }
 
 template <int DT>

@@ -162,6 +162,63 @@ __device__ __forceinline__ void dma_sync() {
 
 // ---------------------------------------------------------------- scheduling
 
+// Persistent heaviest-first (longest-processing-time) schedule over
+// nheads x ntiles work units whose cost depends only on their tile's rank:
+// rank 0 is the heaviest.  The grid's G workgroups take the units, heaviest
+// rank first across all heads, in rounds of G whose direction alternates
+// (round r: workgroup w takes unit r G + w when r is even, r G + G - 1 - w
+// when odd), so that each workgroup's heavy and light units pair up and all
+// end with nearly the same total.  With `pin` (heads and grid both split
+// evenly over the 8 XCDs) each XCD keeps its own heads: head x + 8 i runs on
+// XCD x (workgroups w with w % 8 == x), so a head's operands stay in one L2.
+// run(head, rank) is called once per unit of this workgroup.
+template <typename F>
+__device__ __forceinline__ void lpt_units(int ntiles, int nheads, bool pin, F&& run) {
+  constexpr int kXcd = 8;
+  const int w = blockIdx.x;
+  const int G = gridDim.x;
+  int v, g, heads, x;
+  if (pin) {
+    x = w % kXcd;
+    v = w / kXcd;
+    g = G / kXcd;
+    heads = nheads / kXcd;
+  } else {
+    x = 0;
+    v = w;
+    g = G;
+    heads = nheads;
+  }
+  const int units = heads * ntiles;
+  for (int r = 0; r * g < units; ++r) {
+    const int k = r * g + ((r & 1) ? g - 1 - v : v);
+    if (k < units) {
+      const int hi = k % heads;
+      run(pin ? x + kXcd * hi : hi, k / heads);
+    }
+  }
+}
+
+// Workgroups of `kernel` (with `threads` threads) resident at once on the
+// current device, cached per device and kernel; 0 if it cannot be queried.
+template <typename K>
+int resident_slots(K kernel, int threads) {
+  constexpr int kMaxDev = 64;
+  static int cache[kMaxDev];  // written once per device with the same value
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDev && __atomic_load_n(&cache[dev], __ATOMIC_RELAXED) > 0)
+    return __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
+    return 0;
+  const int slots = cus * per_cu;
+  if (dev < kMaxDev) __atomic_store_n(&cache[dev], slots, __ATOMIC_RELAXED);
+  return slots;
+}
+
 // MI355X dispatches consecutive workgroup ids round-robin over its 8 XCDs,
 // each with a private L2.  Remap so that a contiguous range of logical ids
 // (the query tiles of one head, which stream the same K/V) runs on one XCD.

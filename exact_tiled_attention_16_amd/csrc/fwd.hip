@@ -29,7 +29,6 @@
 //   O^T += V_j^T P^T on matrix cores, V read from LDS by transposed 16-bit
 //     reads; O^T has one query per lane, so the rescale is a per-lane multiply.
 #include <algorithm>
-#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -58,48 +57,9 @@ __device__ __forceinline__ int swz(int r) {
 // QB = query blocks of 32 rows per wave; OCC = waves per SIMD the register
 // budget is sized for (1: 512 registers, 2: 256); NSTG = LDS stages per
 // tensor (2 or 3, see the pipeline description below).
-// Persistent causal schedule.  A causal query tile qt costs qt + 1 key
-// tiles, so the units are taken heaviest first (longest-processing-time
-// order): unit k of a list holds query tile n_qtiles - 1 - k / heads of head
-// k % heads.  The grid's G workgroups take the list in rounds of G, in
-// alternating direction (round r: workgroup w takes unit r G + w when r is
-// even, r G + G - 1 - w when odd), so that each workgroup's heavy and light
-// units pair up and every workgroup ends with nearly the same total.  When
-// the heads and the grid both split evenly over the 8 XCDs (a.pin), each XCD
-// keeps its own heads (head x + 8 i on XCD x, which runs workgroups w with
-// w % 8 == x) so that a head's K and V stay in one L2.
-template <typename F>
-__device__ __forceinline__ void persistent_units(const FwdArgs& a, F&& run) {
-  constexpr int kXcd = 8;
-  const int w = blockIdx.x;
-  const int G = gridDim.x;
-  const int nq = a.n_qtiles;
-  int v, g, heads, x;
-  if (a.pin) {
-    x = w % kXcd;
-    v = w / kXcd;
-    g = G / kXcd;
-    heads = a.bh / kXcd;
-  } else {
-    x = 0;
-    v = w;
-    g = G;
-    heads = a.bh;
-  }
-  const int units = heads * nq;
-  for (int r = 0; r * g < units; ++r) {
-    const int k = r * g + ((r & 1) ? g - 1 - v : v);
-    if (k < units) {
-      const int qt = nq - 1 - k / heads;
-      const int hi = k % heads;
-      run(a.pin ? x + kXcd * hi : hi, qt);
-    }
-  }
-}
-
 // PERSIST: the grid holds one workgroup per resident slot, and each loops
-// over the work units (b, h, query tile) of a fixed causal schedule (see
-// persistent_units below); otherwise each workgroup takes one unit.
+// over the work units (b, h, query tile) of the causal heaviest-first
+// schedule (lpt_units); otherwise each workgroup takes one unit.
 // PARTIAL: split-KV mode.  Unit (b, h, query tile, split s) attends to keys
 // [s k_chunk, (s+1) k_chunk) only and writes O normalised over those keys in
 // fp32 and their log-sum-exp to slot s of the partial outputs; a merge kernel
@@ -585,8 +545,9 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
   };  // unit
 
   if constexpr (PERSIST) {
-    persistent_units(a, [&](int bh, int qt) {
-      unit(bh, qt, 0);
+    // A causal query tile qt costs qt + 1 key tiles: rank 0 is the last one.
+    lpt_units(a.n_qtiles, a.bh, a.pin != 0, [&](int bh, int rank) {
+      unit(bh, a.n_qtiles - 1 - rank, 0);
       // The next unit's first copies reuse the ring: every wave must be done
       // reading it (this wave's own copies have all landed already).
       __builtin_amdgcn_s_barrier();
@@ -650,16 +611,6 @@ int sparse_list_stride(int N) {
   return (N + FwdSparseCfg<D>::BN - 1) / FwdSparseCfg<D>::BN + 2 + kSparsePad;
 }
 
-// Workgroups of `kernel` resident at once on the current device.
-template <typename K>
-int query_resident_slots(K kernel, int threads) {
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
-  return cus * per_cu;
-}
-
 template <int D, bool CAUSAL, bool PERSIST, bool PARTIAL, int DT, bool SPARSE = false,
           class C = FwdCfg<D>>
 hipError_t launch_one(const FwdArgs& a, int BH, hipStream_t stream,
@@ -674,16 +625,7 @@ hipError_t launch_one(const FwdArgs& a, int BH, hipStream_t stream,
       fwd_kernel<D, C::BN, C::NW, C::QB, C::OCC, C::NSTG, CAUSAL, DT, PERSIST, PARTIAL, SPARSE>;
   int64_t grid = units;
   if constexpr (PERSIST) {
-    // Device property cache, filled once per device and instantiation.
-    constexpr int kMaxDev = 16;
-    static std::atomic<int> cache[kMaxDev];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidValue;
-    int slots = dev < kMaxDev ? cache[dev].load(std::memory_order_relaxed) : 0;
-    if (slots <= 0) {
-      slots = query_resident_slots(kernel, C::NW * 64);
-      if (dev < kMaxDev) cache[dev].store(slots, std::memory_order_relaxed);
-    }
+    const int slots = resident_slots(kernel, C::NW * 64);
     if (slots <= 0) return hipErrorInvalidValue;
     grid = std::min<int64_t>(units, slots);
     args.pin = (BH % 8 == 0 && grid % 8 == 0) ? 1 : 0;

@@ -77,6 +77,8 @@ struct BwdArgs {
   void* dv;
   int N;
   int n_ktiles;      // filled in by the launcher
+  int bh;            // B * H (launcher)
+  int pin;           // persistent schedule keeps each head on one XCD (launcher)
   float scale;
   float scale_log2;
 };

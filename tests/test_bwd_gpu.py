@@ -129,3 +129,32 @@ def test_backward_repeatable():
         torch.cuda.synchronize()
         assert torch.equal(r[0], r0[0]), "dQ differs between calls"
         assert torch.equal(r[1], r0[1]) and torch.equal(r[2], r0[2])
+
+
+@pytest.mark.parametrize("B,H,N,d", [(2, 8, 2048, 128),   # 16 heads: pinned to XCDs
+                                     (3, 7, 3000, 128),   # 21 heads: unpinned, ragged
+                                     (1, 5, 1000, 64)])   # fewer units than slots
+def test_causal_persistent_schedule_writes_every_unit(B, H, N, d):
+    """The causal backward runs both main kernels on a persistent grid that
+    walks the units heaviest first; every dQ, dK and dV element must be
+    written (the outputs start as NaN) and the first and last heads must
+    match the oracle."""
+    import torch
+    fa = _fa()
+    _banner(f"causal persistent B={B} H={H} N={N} d={d}")
+    q, k, v = inputs.qkv(B, H, N, d, 80 + N)
+    do = inputs.dout(B, H, N, d, 80 + N)
+    (qt, q64), (kt, k64), (vt, v64), (dot, do64) = (host_round(x, "bf16") for x in (q, k, v, do))
+    qd, kd, vd, dod = (to_device(t) for t in (qt, kt, vt, dot))
+    o, lse = fa.fwd(qd, kd, vd, causal=True)
+    dq = torch.full((B, H, N, d), float("nan"), dtype=torch.float32, device="cuda")
+    dk = torch.full_like(qd, float("nan"))
+    dv = torch.full_like(qd, float("nan"))
+    fa.bwd(qd, kd, vd, o, lse, dod, causal=True, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert not torch.isnan(t).any(), name
+    got = tuple(x.to(torch.float64).cpu().numpy() for x in (dq, dk, dv))
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        _check(got, (q64, k64, v64, do64), f"head ({b},{h})", True,
+               sl=(slice(b, b + 1), slice(h, h + 1)))
