@@ -29,6 +29,8 @@
 //     addressed by lane 2e + j/8); 16-byte chunks of a V row are XOR-swizzled
 //     so that the eight rows those reads touch fall in distinct LDS banks, and
 //     K rows so that sixteen rows read at one column do.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -77,7 +79,7 @@ __device__ __forceinline__ int k_swz(int row) {
 // NSTG = LDS stages per tensor: 8 runs the iterations in groups of four with
 // one workgroup barrier per group, 3 has one barrier per iteration (see
 // below).
-template <int D, int BN, int NW, int OCC, int NSTG, bool CAUSAL>
+template <int D, int BN, int NW, int OCC, int NSTG, bool CAUSAL, bool PERSIST>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
   constexpr int BM = 32 * NW;
@@ -99,17 +101,19 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NSTG * TILEB];
   FA_LDS uint8_t* lds = (FA_LDS uint8_t*)smem;  // K stage s at s*TILEB, V at (NSTG+s)*TILEB
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hl = lane >> 5;
-  const int l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int N = a.N;
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / a.n_qtiles;
-  int qt = logical % a.n_qtiles;
-  if (CAUSAL) qt = a.n_qtiles - 1 - qt;
+  // One work unit: query tile qt of head bh.
+  auto unit = [&](const int bh, const int qt) __attribute__((always_inline)) {
+  // In the persistent loop the lane index passes through an empty asm so
+  // that nothing derived from it is hoisted out of the loop over units (it
+  // would stay live across units and spill at the register limit).
+  int tid = threadIdx.x;
+  if constexpr (PERSIST) asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int hl = lane >> 5;
+  const int l32 = lane & 31;
   const int64_t base = (int64_t)bh * N * D;
   const uint8_t* Q = static_cast<const uint8_t*>(a.q8) + base;
   const uint8_t* K = static_cast<const uint8_t*>(a.k8) + base;
@@ -537,17 +541,51 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
     if (hl == 0 && a.lse != nullptr)
       a.lse[(int64_t)bh * N + qrow] = m_run * kLn2 + __logf(l_tot);
   }
+  };  // unit
+
+  if constexpr (PERSIST) {
+    // Causal: query tile qt costs qt + 1 key tiles; rank 0 is the last one.
+    lpt_units(a.n_qtiles, a.bh, a.pin != 0, [&](int bh, int rank) {
+      unit(bh, a.n_qtiles - 1 - rank);
+      // The next unit's first copies reuse the ring.
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    });
+  } else {
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    int qt = logical % a.n_qtiles;
+    if (CAUSAL) qt = a.n_qtiles - 1 - qt;  // longest key ranges first
+    unit(logical / a.n_qtiles, qt);
+  }
 }
 
+// Causal launches walk the units on a persistent heaviest-first grid at
+// d = 128 and 256 (+4 to +21 % over one workgroup per tile); at d = 64 that
+// measured 35 % slower (two 128-row workgroups per CU: 64 concurrent units
+// of an XCD spread over eight heads' keys and values instead of one head's,
+// at the lowest arithmetic intensity), so d = 64 keeps one workgroup per
+// tile in dispatch order.
 template <int D, int NW, int OCC, int NSTG, bool CAUSAL>
 hipError_t launch_one(const Fp8Args& a0, int BH, hipStream_t s) {
   constexpr int BM = 32 * NW;
+  constexpr bool PERSIST = CAUSAL && D >= 128;
   Fp8Args a = a0;
   a.n_qtiles = (a.N + BM - 1) / BM;
-  const int64_t grid = (int64_t)a.n_qtiles * BH;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_fp8_kernel<D, 64, NW, OCC, NSTG, CAUSAL>), dim3((unsigned)grid),
-                     dim3(NW * 64), 0, s, a, a.k_scale, a.v_scale);
+  a.bh = BH;
+  const int64_t units = (int64_t)a.n_qtiles * BH;
+  if (units > 0x7fffffff) return hipErrorInvalidValue;
+  if constexpr (!PERSIST) {
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, 64, NW, OCC, NSTG, CAUSAL, false>),
+                       dim3((unsigned)units), dim3(NW * 64), 0, s, a, a.k_scale, a.v_scale);
+  } else {
+    auto kernel = fwd_fp8_kernel<D, 64, NW, OCC, NSTG, true, true>;
+    const int slots = resident_slots(kernel, NW * 64);
+    if (slots <= 0) return hipErrorInvalidValue;
+    const int64_t grid = std::min<int64_t>(units, slots);
+    a.pin = (BH % 8 == 0 && grid % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(NW * 64), 0, s, a, a.k_scale,
+                       a.v_scale);
+  }
   return hipGetLastError();
 }
 

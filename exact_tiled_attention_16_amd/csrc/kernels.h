@@ -108,6 +108,8 @@ struct Fp8Args {
   int N;
   int nblk;
   int n_qtiles;          // filled in by the launcher
+  int bh;                // B * H (launcher)
+  int pin;               // persistent schedule keeps each head on one XCD (launcher)
   float scale_log2;
 };
 

@@ -210,3 +210,25 @@ def test_fp8_error_lower_than_per_tensor_baseline():
     print(f"  RMSE block+rotation {r['block_rot']:.3e}, per-tensor {r['per_tensor']:.3e}, "
           f"ratio {r['per_tensor'] / r['block_rot']:.2f}x; bf16 path {r['bf16']:.3e}")
     assert r["block_rot"] < r["per_tensor"]
+
+
+@pytest.mark.parametrize("B,H,N,d", [(2, 8, 2048, 128),   # 16 heads: pinned to XCDs
+                                     (3, 7, 3000, 128),   # 21 heads: unpinned, ragged
+                                     (1, 3, 700, 64),     # fewer units than slots
+                                     (1, 5, 1500, 256)])  # one wave per SIMD
+def test_causal_persistent_schedule_writes_every_unit(B, H, N, d):
+    """The causal fp8 forward runs on a persistent grid that walks the units
+    heaviest first; every output element must be written (O and LSE start
+    as NaN) and the first and last heads must pass the parity gates."""
+    import torch
+    fa = _fa()
+    _banner(f"fp8 causal persistent B={B} H={H} N={N} d={d}")
+    ops = _oracle_operands(B, H, N, d, 90 + N)
+    q8, k8, v8, qs, ks, vs = (torch.from_numpy(np.ascontiguousarray(x)).to("cuda") for x in ops)
+    o = torch.full((B, H, N, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
+    fa.fwd_fp8(q8, k8, v8, qs, ks, vs, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any()
+    _check_fp8_heads(ops, o.to(torch.float64).cpu().numpy(), lse.to(torch.float64).cpu().numpy(),
+                     ((0, 0), (B - 1, H - 1)), True, f"N={N} d={d}")
