@@ -135,9 +135,17 @@ __device__ __forceinline__ u32x4_t make_rsrc(const void* base, int bytes) {
 // therefore tracked only by the explicit vector-memory waits below, which
 // also order the compiler's own loads correctly (vector-memory operations
 // complete in issue order).
+// The statement also supplies its own wait states: a vector-memory
+// instruction reading an SGPR that a vector ALU instruction wrote (the
+// descriptor fields pass through v_readfirstlane, or come back from a spill
+// by v_readlane) needs five, and an LDS-DMA load after a scalar write of M0
+// needs one.  The compiler inserts these before its own memory instructions
+// but cannot see into an asm statement, so without them the load may take a
+// stale base address or M0.  s_nop 4 gives five.
 __device__ __forceinline__ void dma16_buf(u32x4_t r, uint32_t voff, FA_LDS void* lds_block) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_block);
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "{m0}"(m0) : "memory");
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               : : "v"(voff), "s"(r), "{m0}"(m0) : "memory");
 }
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
