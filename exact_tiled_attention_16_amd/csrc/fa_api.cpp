@@ -214,13 +214,14 @@ int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, flo
 }
 
 int fa_quant_fp8(const void* x, int dtype, void* x8, float* scales, const float* signs,
-                 float scale_mul, int per_tensor, int B, int H, int N, int d, void* stream) {
+                 float scale_mul, int mode, int B, int H, int N, int d, void* stream) {
   if (!x || !x8 || !scales) return FA_ERR_INVALID;
   if (!aligned16(x) || !aligned16(x8) || !aligned4(scales) || !aligned4(signs))
     return FA_ERR_INVALID;
   if (!valid_scale(scale_mul)) return FA_ERR_INVALID;
   if (!valid_dims(B, H, N) || (dtype != FA_BF16 && dtype != FA_FP16)) return FA_ERR_INVALID;
-  if (per_tensor != 0 && per_tensor != 1) return FA_ERR_INVALID;
+  if (mode != FA_FP8_BLOCK_SCALES && mode != FA_FP8_TENSOR_SCALE && mode != FA_FP8_BLOCK_POW2)
+    return FA_ERR_INVALID;
   if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
   fa::QuantArgs a{};
   a.x = x;
@@ -231,8 +232,8 @@ int fa_quant_fp8(const void* x, int dtype, void* x8, float* scales, const float*
   a.N = N;
   a.nblk = (N + FA_FP8_BLOCK - 1) / FA_FP8_BLOCK;
   if ((int64_t)B * H * a.nblk > 0x7fffffff) return FA_ERR_INVALID;
-  return launch_status(fa::launch_quant_fp8(a, B, H, d, dtype, per_tensor != 0,
-                                            static_cast<hipStream_t>(stream)));
+  return launch_status(
+      fa::launch_quant_fp8(a, B, H, d, dtype, mode, static_cast<hipStream_t>(stream)));
 }
 
 int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_scale,

@@ -19,11 +19,14 @@
 //     tile exceeds kLazySum8 = 448, so every P~ stays at most 448 (the e4m3
 //     maximum: no saturation); the row normaliser is summed from the fp32
 //     P~;
-//   * the output accumulator is kept in units of one value block's scale;
-//     when the next P V product uses another block (every 128 keys) it is
-//     multiplied by vs_old / vs_new under the matrix products of the
-//     iteration before, and by the factor of a reference raise at the end of
-//     a tile;
+//   * the output accumulator is kept in units of one value block's scale
+//     vs_acc; a later block whose scale differs from vs_acc by a power of two
+//     (power-of-two block scales, or one scale per tensor) has that factor
+//     applied as the e4m3 operand's block-scale exponent of its P V products
+//     (the scaled matrix instruction's E8M0 scale: exact, no vector work);
+//     any other block scale re-expresses O by vs_acc / vs_new under the
+//     matrix products of the iteration before, and a reference raise
+//     rescales O at the end of a tile;
 //   * V8 stays row-major in LDS and is read transposed with ds_read_b64_tr_b8
 //     (inside a 16-lane group, lane j's byte e is byte j%8 of the chunk
 //     addressed by lane 2e + j/8); 16-byte chunks of a V row are XOR-swizzled
@@ -48,6 +51,13 @@ typedef int i32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ f32x16_t mfma_fp8(i32x8_t a, i32x8_t b, f32x16_t c) {
   // Format code 0 = e4m3 for both operands; no per-block hardware scaling.
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// The same product with A's elements multiplied by 2^(ea - 127): an E8M0
+// block scale (lane l's value covers row l % 32 over its 32 K slots; here the
+// same value in every lane), B's scale 127 = 1.
+__device__ __forceinline__ f32x16_t mfma_fp8_scale_a(i32x8_t a, i32x8_t b, f32x16_t c, int ea) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, ea, 0, 127);
 }
 
 __device__ __forceinline__ i32x2_t ld_lds_tr8(const FA_LDS void* p) {
@@ -280,12 +290,24 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   auto vscale_ratio = [](float from, float to) {
     return from == to ? 1.0f : from * __builtin_amdgcn_rcpf(to);
   };
+  // E8M0 exponent that carries `to` relative to `from` (127 + the exponent
+  // difference) when both are normal fp32 values with equal mantissas and
+  // the difference fits the E8M0 range; -1 otherwise.
+  auto vscale_exponent = [](float from, float to) {
+    const uint32_t a = __float_as_uint(from), b = __float_as_uint(to);
+    const int ea = (int)((a >> 23) & 0xffu), eb = (int)((b >> 23) & 0xffu);
+    const int x = 127 + eb - ea;
+    const bool ok = ((a ^ b) & 0x807fffffu) == 0 && ea != 0 && eb != 0 && x >= 0 && x <= 254;
+    return ok ? x : -1;
+  };
 
   // ---- End of a tile: raise the reference if the tile's probabilities left
-  // [0, kLazySum8] (or the row had none), and re-express O in the V scale of
-  // the next P V product.  O already holds P(j-1) V(j-1).
+  // [0, kLazySum8] (or the row had none), rescaling O (which already holds
+  // P(j-1) V(j-1)) and l to the new reference.
   const uint32_t opaque_zero = (uint32_t)(N >> 31);
-  auto finish_tile = [&](const Scores& s, Probs& pw, float mul, float psum, float vs_next) {
+  // `extra`: a value-block factor for O still to apply (one wave per SIMD
+  // re-expresses O here rather than under the matrix products), else 1.
+  auto finish_tile = [&](const Scores& s, Probs& pw, float mul, float psum, float extra) {
     float alpha = 1.0f;
     if (wave_any(!(psum <= kLazySum8))) {
       asm volatile("" ::: "memory");
@@ -307,8 +329,8 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
       for (int w = 0; w < 8; ++w) pw[w] = (int)((uint32_t)fresh[w] | ((uint32_t)pw[w] & opaque_zero));
     }
     l_run += psum;
-    const float f = alpha * vscale_ratio(vs_acc, vs_next);
-    if (f != 1.0f) {  // wave-uniform: alpha is 1 unless a raise happened
+    const float f = alpha * extra;
+    if (f != 1.0f) {  // wave-uniform; rare
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int i = 0; i < NDB; ++i)
@@ -324,7 +346,6 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
           }
         }
     }
-    vs_acc = vs_next;
   };
 
   // Fused iteration (see the 16-bit forward): NSTEP steps, each with one
@@ -338,11 +359,12 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   // the steps would also wait for every fragment read in flight.
   float ks_pre = kscale(-1), vs_pre = vscale(-1);
   // VB: tile j starts a value block (j even: 128-row blocks of two 64-key
-  // tiles).  Then, once P(j-1) V(j-1) has been issued, O is re-expressed in
-  // the new block's scale by multiplying it by vs_acc / vs_j during the last
-  // S(j+1) steps, where the matrix work hides the multiplies, before P(j)
-  // V(j) is added in the next iteration; the end of the tile then finds the
-  // ratio 1 and only a reference raise rescales there.
+  // tiles).  Its scale vs_j is carried either by the E8M0 exponent ea_cur of
+  // the P V products of the block (when vs_j = 2^k vs_acc), or, once P(j-1)
+  // V(j-1) has been issued, by re-expressing O in vs_j: O times vs_acc / vs_j
+  // during the last S(j+1) steps, where the matrix work hides the
+  // multiplies, before P(j) V(j) is added in the next iteration.
+  int ea_cur = 127;  // E8M0 exponent of the value block of the P V products
   auto issue_iter = [&](int j, int st) {
     issue(K, j + 3, lds + st * TILEB, koff_dma);
     issue(V, j + 1, lds + (NSTG + snext(st)) * TILEB, voff_dma);
@@ -368,10 +390,17 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
     const FA_LDS uint8_t* vs = lds + (NSTG + (GROUPED ? (j - 1) & MSK : sprev(st))) * TILEB;
     const float mul = qmul * ks_j;  // tile j's scores to log2 units
     const float m_neg = -m_run;
+    const int ea_pv = ea_cur;  // P(j-1) V(j-1): the previous tile's block
     float vratio = 1.0f;
     if constexpr (VB) {
-      vratio = vscale_ratio(vs_acc, vs_j);
-      vs_acc = vs_j;
+      const int x = vscale_exponent(vs_acc, vs_j);
+      if (x >= 0) {
+        ea_cur = x;
+      } else {
+        vratio = vscale_ratio(vs_acc, vs_j);
+        vs_acc = vs_j;
+        ea_cur = 127;
+      }
     }
     if constexpr (DS) {
 #pragma unroll
@@ -406,7 +435,7 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
           if (m + PF < M1) fr[(m + PF - M0) % (PF + 1)] = frag(m + PF);
           const i32x8_t& f = fr[(m - M0) % (PF + 1)];
           if (m < NS_PV) {
-            oacc[m] = mfma_fp8(f, pf, oacc[m]);
+            oacc[m] = mfma_fp8_scale_a(f, pf, oacc[m], ea_pv);
           } else {
             const int kb = (m - NS_PV) / NDC, dc = (m - NS_PV) % NDC;
             s_nxt[kb] = mfma_fp8(f, qf[dc], s_nxt[kb]);
@@ -426,10 +455,11 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
           p_cur[w] = pack4(p[0], p[1], p[2], p[3], p_cur[w]);
         }
       }
-      if constexpr (VB) {
+      if constexpr (VB && OCC > 1) {
         // The last half of the steps: O blocks 2 (step - NSTEP/2) .. +1,
-        // whose products were issued at least NSTEP/2 steps earlier.
-        if (step >= NSTEP / 2) {
+        // whose products were issued at least NSTEP/2 steps earlier (skipped,
+        // wave-uniformly, when the exponent carries the block scale).
+        if (step >= NSTEP / 2 && vratio != 1.0f) {
           constexpr int PER = NDB / (NSTEP - NSTEP / 2);
 #pragma unroll
           for (int i = 0; i < PER; ++i)
@@ -457,7 +487,7 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
             if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s_nxt[kb][r] = -INFINITY;
       }
     }
-    if constexpr (DP) finish_tile(s_cur, p_cur, mul, ps0 + ps1, vs_j);
+    if constexpr (DP) finish_tile(s_cur, p_cur, mul, ps0 + ps1, OCC > 1 ? 1.0f : vratio);
     if constexpr (!GROUPED)
       dma_sync<2 * IPW>();
     else if constexpr (POS == -1 || POS == G - 1)

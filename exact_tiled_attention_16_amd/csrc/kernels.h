@@ -93,7 +93,9 @@ struct QuantArgs {
   int nblk;            // ceil(N / 128)
 };
 
-hipError_t launch_quant_fp8(const QuantArgs& a, int B, int H, int d, int dtype, bool per_tensor,
+// mode: 0 block scales, 1 one scale per tensor, 2 block scales rounded up
+// to a power of two.
+hipError_t launch_quant_fp8(const QuantArgs& a, int B, int H, int d, int dtype, int mode,
                             hipStream_t stream);
 
 struct Fp8Args {

@@ -7,7 +7,8 @@
 //        Hadamard matrix, applied by the fast Walsh-Hadamard transform in
 //        fp32 with half-widths 1, 2, ..., d/2 in that order; each level maps
 //        the pair (x[i], x[i+h]), i & h == 0, to (x[i] + x[i+h], x[i] - x[i+h]))
-//   scale = amax(|x'| over the block) / 448   (1 when the amax is 0)
+//   scale = amax(|x'| over the block) / 448   (1 when the amax is 0), or in
+//           the power-of-two mode that value rounded up to a power of two
 //   code  = e4m3_rne(clamp(x' / scale, -448, 448)),  stored = scale * scale_mul
 //
 // A block is FA_FP8_BLOCK = 128 rows of one (b, h), all d columns.  Each row is
@@ -61,8 +62,21 @@ __device__ __forceinline__ float lane_xor_in_quad(float v) {
                                                         0xF, false));
 }
 
+// Smallest power of two >= s for a positive finite fp32 s, from its bits: a
+// power of two keeps its value; a normal value goes to the next exponent; a
+// subnormal one to the next power of two above its mantissa (2^-126 at most).
+__device__ __forceinline__ float pow2_ceil_f32(float s) {
+  const uint32_t b = __float_as_uint(s);
+  const uint32_t man = b & 0x007fffffu;
+  const uint32_t ex = b & 0x7f800000u;
+  if (ex != 0) return man == 0 ? s : __uint_as_float(ex + 0x00800000u);
+  if ((man & (man - 1u)) == 0) return s;
+  return __uint_as_float(1u << (32 - __builtin_clz(man)));
+}
+
 // MODE 0: block scales, quantise.  MODE 1: write the block amax only.
 // MODE 2: quantise with the amax found in scales[slot] (per-tensor mode).
+// MODE 3: block scales rounded up to a power of two, quantise.
 template <int D, int DT, int MODE>
 __global__ void __launch_bounds__(quant_threads<D>())
 quant_kernel(QuantArgs a) {
@@ -166,16 +180,19 @@ quant_kernel(QuantArgs a) {
     }
   }
 
-  const float scale = block_amax > 0.f ? block_amax / 448.0f : 1.0f;
+  float scale = block_amax > 0.f ? block_amax / 448.0f : 1.0f;
+  if constexpr (MODE == 3) scale = pow2_ceil_f32(scale);  // x' / scale then exact
   // x / scale correctly rounded (IEEE division) from the correctly rounded
   // reciprocal and one residual step: for q0 within 1 ulp of x / scale and
   // rinv within half an ulp of 1 / scale, q0 + fma(-q0, scale, x) * rinv is
   // the correctly rounded quotient (Markstein, IBM J. Res. Dev. 34(1), 1990)
-  // outside the subnormal range, where every code is zero anyway.
+  // outside the subnormal range, where every code is zero anyway.  The
+  // quotient has the sign of x' (scale > 0); the residual step alone would
+  // turn -0 into +0, so the sign is put back.
   const float rinv = 1.0f / scale;
   auto quotient = [&](float v) {
     const float q0 = v * rinv;
-    return fmaf(fmaf(-q0, scale, v), rinv, q0);
+    return __builtin_copysignf(fmaf(fmaf(-q0, scale, v), rinv, q0), v);
   };
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
@@ -219,12 +236,16 @@ reduce_max_kernel(float* v, int n) {
 }
 
 template <int D, int DT>
-hipError_t launch_d(const QuantArgs& a, int BH, bool per_tensor, hipStream_t s) {
+hipError_t launch_d(const QuantArgs& a, int BH, int mode, hipStream_t s) {
   const int64_t grid = (int64_t)BH * a.nblk;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  if (!per_tensor) {
-    hipLaunchKernelGGL((quant_kernel<D, DT, 0>), dim3((unsigned)grid), dim3(quant_threads<D>()), 0,
-                       s, a);
+  if (mode != 1) {
+    if (mode == 2)
+      hipLaunchKernelGGL((quant_kernel<D, DT, 3>), dim3((unsigned)grid), dim3(quant_threads<D>()),
+                         0, s, a);
+    else
+      hipLaunchKernelGGL((quant_kernel<D, DT, 0>), dim3((unsigned)grid), dim3(quant_threads<D>()),
+                         0, s, a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((quant_kernel<D, DT, 1>), dim3((unsigned)grid), dim3(quant_threads<D>()), 0, s,
@@ -240,22 +261,22 @@ hipError_t launch_d(const QuantArgs& a, int BH, bool per_tensor, hipStream_t s) 
 }
 
 template <int DT>
-hipError_t launch_dtype(const QuantArgs& a, int BH, int d, bool per_tensor, hipStream_t s) {
+hipError_t launch_dtype(const QuantArgs& a, int BH, int d, int mode, hipStream_t s) {
   switch (d) {
-    case 64: return launch_d<64, DT>(a, BH, per_tensor, s);
-    case 128: return launch_d<128, DT>(a, BH, per_tensor, s);
-    case 256: return launch_d<256, DT>(a, BH, per_tensor, s);
+    case 64: return launch_d<64, DT>(a, BH, mode, s);
+    case 128: return launch_d<128, DT>(a, BH, mode, s);
+    case 256: return launch_d<256, DT>(a, BH, mode, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_quant_fp8(const QuantArgs& a, int B, int H, int d, int dtype, bool per_tensor,
+hipError_t launch_quant_fp8(const QuantArgs& a, int B, int H, int d, int dtype, int mode,
                             hipStream_t stream) {
   const int BH = B * H;
-  return dtype == 0 ? launch_dtype<0>(a, BH, d, per_tensor, stream)
-                    : launch_dtype<1>(a, BH, d, per_tensor, stream);
+  return dtype == 0 ? launch_dtype<0>(a, BH, d, mode, stream)
+                    : launch_dtype<1>(a, BH, d, mode, stream);
 }
 
 }  // namespace fa

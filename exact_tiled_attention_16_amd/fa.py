@@ -28,6 +28,9 @@ BWD_NOALLOC_MAX_ROWS = 2097152
 FA_BF16 = 0
 FA_FP16 = 1
 FP8_BLOCK = 128
+FA_FP8_BLOCK_SCALES = 0
+FA_FP8_TENSOR_SCALE = 1
+FA_FP8_BLOCK_POW2 = 2
 
 # Every symbol include/fa.h declares, with (restype, argtypes).
 _P = ctypes.c_void_p
@@ -108,10 +111,10 @@ def fa_testing_fwd_per_tile(q, k, v, o, lse, B, H, N, d, dtype, scale, causal,
                                          scale, causal, stream)
 
 
-def fa_quant_fp8(x, dtype, x8, scales, signs, scale_mul, per_tensor, B, H, N,
-                 d, stream) -> int:
-    return lib().fa_quant_fp8(x, dtype, x8, scales, signs, scale_mul,
-                              per_tensor, B, H, N, d, stream)
+def fa_quant_fp8(x, dtype, x8, scales, signs, scale_mul, mode, B, H, N, d,
+                 stream) -> int:
+    return lib().fa_quant_fp8(x, dtype, x8, scales, signs, scale_mul, mode, B,
+                              H, N, d, stream)
 
 
 def fa_fwd_fp8(q8, k8, v8, qs, ks, vs, o, lse, B, H, N, d, scale, causal,
@@ -264,10 +267,15 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
 
 
 def quant_fp8(x, signs=None, scale_mul: float = 1.0, per_tensor: bool = False,
-              out=None, scales=None):
+              out=None, scales=None, pow2: bool = False):
     """e4m3 codes (uint8 [B,H,N,d]) and block scales (float32 [B,H,ceil(N/128)])
     of a bf16/fp16 device tensor; ``signs`` (float32 device tensor of d +-1
-    values) turns on the Hadamard rotation."""
+    values) turns on the Hadamard rotation; ``per_tensor`` uses one scale for
+    the tensor, ``pow2`` rounds the block scales up to powers of two."""
+    if per_tensor and pow2:
+        raise ValueError("pow2 is a block-scale option")
+    mode = (FA_FP8_TENSOR_SCALE if per_tensor
+            else FA_FP8_BLOCK_POW2 if pow2 else FA_FP8_BLOCK_SCALES)
     torch = _torch()
     if x.dim() != 4:
         raise ValueError("x must be [B, H, N, d]")
@@ -286,7 +294,7 @@ def quant_fp8(x, signs=None, scale_mul: float = 1.0, per_tensor: bool = False,
         _check_tensor(signs, "signs", (d,), torch.float32)
         sp = signs.data_ptr()
     _check(fa_quant_fp8(x.data_ptr(), dt, out.data_ptr(), scales.data_ptr(), sp,
-                        float(scale_mul), int(bool(per_tensor)), B, H, N, d, _stream(x)))
+                        float(scale_mul), mode, B, H, N, d, _stream(x)))
     return out, scales
 
 

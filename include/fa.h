@@ -62,6 +62,11 @@ extern "C" {
 /* Rows per fp8 quantisation block (per (b, h), all d columns). */
 #define FA_FP8_BLOCK 128
 
+/* Scale modes of fa_quant_fp8. */
+#define FA_FP8_BLOCK_SCALES 0
+#define FA_FP8_TENSOR_SCALE 1
+#define FA_FP8_BLOCK_POW2 2
+
 /*
  * fa_fwd -- attention forward.
  *   q, k, v : [B][H][N][d] of `dtype` (FA_BF16 or FA_FP16), read only.
@@ -96,15 +101,20 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *               (half-widths 1, 2, ..., d/2 in that order).  NULL = x' = x.
  *   scale_mul : multiplies every stored scale (1/d for a rotated Q, so that
  *               dequantised Q.K equals the unrotated product; else 1).
- *   per_tensor: 0 = one scale per 128-row block of each (b, h);
- *               1 = one scale for the whole tensor, written to every slot.
- *   Scale = amax(|x'|) / 448 in fp32 (1 if the amax is 0), times scale_mul;
- *   code = round-to-nearest-even of x' / (amax/448) in fp32, saturated to
- *   +-448.  Per-tensor mode enqueues three kernels (block amax, reduction
- *   into every slot of `scales`, quantisation); block mode enqueues one.
+ *   mode      : FA_FP8_BLOCK_SCALES (0): one scale per 128-row block of
+ *               each (b, h); FA_FP8_TENSOR_SCALE (1): one scale for the whole
+ *               tensor, written to every slot; FA_FP8_BLOCK_POW2 (2): block
+ *               scales rounded up to the nearest power of two (for V: the
+ *               fp8 forward then applies them as exact exponents of its
+ *               matrix instructions).  Other values: FA_ERR_INVALID.
+ *   Scale = amax(|x'|) / 448 in fp32 (1 if the amax is 0), in mode 2 rounded
+ *   up to a power of two, times scale_mul; code = round-to-nearest-even of
+ *   x' / scale (that scale, before scale_mul) in fp32, saturated to +-448.
+ *   Mode 1 enqueues three kernels (block amax, reduction into every slot of
+ *   `scales`, quantisation); modes 0 and 2 enqueue one.
  */
 int fa_quant_fp8(const void* x, int dtype, void* x8, float* scales,
-                 const float* signs, float scale_mul, int per_tensor,
+                 const float* signs, float scale_mul, int mode,
                  int B, int H, int N, int d, void* stream);
 
 /*
@@ -123,12 +133,19 @@ int fa_quant_fp8(const void* x, int dtype, void* x8, float* scales,
  *   scale, causal     : as in fa_fwd (the ordinary softmax scale).
  *   Errors            : as in fa_fwd (no dtype argument: the codes are
  *                       e4m3, the output bf16).
- * S = Q8 K8^T runs on fp8 matrix-core instructions with fp32 accumulation;
- * block scales are folded into the fp32 scores and into the output
- * rescaling; the probabilities are rounded to e4m3 for the second product
- * while the row normaliser is summed from the fp32 values.  The result is
- * exact attention on the dequantised operands up to that rounding of the
- * probabilities (at most 2^-4 relative per probability) and fp32 rounding.
+ * S = Q8 K8^T runs on fp8 matrix-core instructions with fp32 accumulation
+ * (each instruction aligns the products of 8 consecutive head-dim slots to
+ * the largest of them with 14 bits below its leading bit, so a dominant
+ * product costs the others of its group up to 2^-13 of it); block scales
+ * are folded into the fp32 scores.  Value block scales that differ by
+ * powers of two (FA_FP8_BLOCK_POW2, or one scale per tensor) are applied as
+ * exact exponents of the P V instructions; any other value scales re-express
+ * the output accumulator at each new block (slower, most at d = 256).  The
+ * probabilities are rounded to e4m3 for the second product while the row
+ * normaliser is summed from the fp32 values.  The result is exact attention
+ * on the dequantised operands up to that rounding of the probabilities (at
+ * most 2^-4 relative per probability), the score accumulation and fp32
+ * rounding.
  */
 int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
                const float* q_scale, const float* k_scale,

@@ -83,9 +83,10 @@ def test_fwd_rejects(fa, kw, code):
 
 def test_quant_fp8_rejects(fa):
     base = dict(x=FAKE, dtype=0, x8=FAKE, scales=FAKE, signs=None, scale_mul=1.0,
-                per_tensor=0, B=1, H=1, N=16, d=128, stream=None)
+                mode=0, B=1, H=1, N=16, d=128, stream=None)
     for kw, code in ((dict(x=None), -1), (dict(x8=None), -1), (dict(scales=None), -1),
-                     (dict(N=0), -1), (dict(dtype=5), -1), (dict(per_tensor=3), -1),
+                     (dict(N=0), -1), (dict(dtype=5), -1), (dict(mode=3), -1),
+                     (dict(mode=-1), -1),
                      (dict(d=100), -2), (dict(x=FAKE + 4), -1), (dict(x8=FAKE + 8), -1),
                      (dict(scale_mul=0.0), -1), (dict(scales=FAKE + 2), -1)):
         a = dict(base)
