@@ -4,7 +4,9 @@
 every translation unit under ``csrc/`` to an object in ``_build/`` at the
 repository root and links ``exact_tiled_attention_16_amd/libfa.so`` (and the
 clock probe used by bench.py, ``libfa_probe.so``).  It always
-recompiles; loading code never builds.
+recompiles; loading code never builds.  The device assembly of the sources
+with LDS-DMA copies is checked for the copies' wait states (asmcheck.py);
+a copy without them fails the build.
 """
 
 from __future__ import annotations
@@ -28,6 +30,9 @@ PROBE_LIB = os.path.join(PKG, "libfa_probe.so")
 
 ARCH = "gfx950"
 SOURCES = ["fa_api.cpp", "fwd.hip", "bwd.hip", "quant.hip", "fwd_fp8.hip", "merge.hip"]
+# Sources whose kernels copy tiles with inline-asm LDS-DMA loads: their device
+# assembly is checked for the wait states those copies need (asmcheck.py).
+DMA_SOURCES = ["fwd.hip", "bwd.hip", "fwd_fp8.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",
@@ -67,6 +72,30 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+def _check_asm(src: str, verbose: bool) -> int:
+    """Compile `src`'s device code to assembly and check every LDS-DMA copy;
+    returns the number of copies."""
+    from exact_tiled_attention_16_amd import asmcheck
+    asm = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".s")
+    cmd = [_hipcc(), *COMMON_FLAGS, "--cuda-device-only", "-S", "-x", "hip",
+           os.path.join(CSRC, src), "-o", asm]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{res.stdout}{res.stderr}")
+    with open(asm) as f:
+        text = f.read()
+    problems = asmcheck.check_text(text)
+    if problems:
+        raise RuntimeError(f"{src}: LDS-DMA copies without their wait states:\n"
+                           + "\n".join(problems[:20]))
+    n = asmcheck.copies(text)
+    if n == 0:
+        raise RuntimeError(f"{src}: no LDS-DMA copies found in the device assembly")
+    return n
+
+
 def _link(objs, out, verbose):
     tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
@@ -81,7 +110,10 @@ def _link(objs, out, verbose):
 def build(verbose: bool = False, jobs: int = 8) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
+        checks = [ex.submit(_check_asm, s, verbose) for s in DMA_SOURCES]
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + [PROBE_SOURCE]))
+        for c in checks:
+            c.result()
     _link([os.path.join(OBJDIR, os.path.splitext(PROBE_SOURCE)[0] + ".o")], PROBE_LIB, verbose)
     _link(objs[:len(SOURCES)], LIB, verbose)
     return LIB

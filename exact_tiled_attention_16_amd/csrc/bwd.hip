@@ -186,7 +186,10 @@ bwd_kv3_kernel(BwdArgs a) {
   auto copy_rows = [&](const uint16_t* src, int r0, FA_LDS uint8_t* dst) {
     const u32x4_t r = make_rsrc(src + (int64_t)max(r0, 0) * D, tile_rows(r0) * ROWB);
 #pragma unroll
-    for (int jj = 0; jj < IPW; ++jj) dma16_buf(r, dma_voff[jj], dst + (wave * IPW + jj) * 1024);
+    for (int jj = 0; jj < IPW; ++jj) {
+      if (jj == 0) dma16_buf<4>(r, dma_voff[jj], dst + (wave * IPW + jj) * 1024);
+      else dma16_buf<0>(r, dma_voff[jj], dst + (wave * IPW + jj) * 1024);
+    }
   };
   auto issue_tile = [&](int i, int st) {
     FA_LDS uint8_t* sb = lds + st * STAGEB;
@@ -517,8 +520,13 @@ bwd_dq_kernel(BwdArgs a) {
     const u32x4_t rv = make_rsrc(Vg + (int64_t)t * BN * D, rows * ROWB);
 #pragma unroll
     for (int jj = 0; jj < IPW; ++jj) {
-      dma16_buf(rk, dma_voff[jj], lds + st * TILEB + (wave * IPW + jj) * 1024);
-      dma16_buf(rv, dma_voff[jj], lds + (NSTG + st) * TILEB + (wave * IPW + jj) * 1024);
+      if (jj == 0) {
+        dma16_buf<4>(rk, dma_voff[jj], lds + st * TILEB + (wave * IPW + jj) * 1024);
+        dma16_buf<4>(rv, dma_voff[jj], lds + (NSTG + st) * TILEB + (wave * IPW + jj) * 1024);
+      } else {
+        dma16_buf<0>(rk, dma_voff[jj], lds + st * TILEB + (wave * IPW + jj) * 1024);
+        dma16_buf<0>(rv, dma_voff[jj], lds + (NSTG + st) * TILEB + (wave * IPW + jj) * 1024);
+      }
     }
   };
 

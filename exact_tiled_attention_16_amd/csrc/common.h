@@ -141,11 +141,18 @@ __device__ __forceinline__ u32x4_t make_rsrc(const void* base, int bytes) {
 // by v_readlane) needs five, and an LDS-DMA load after a scalar write of M0
 // needs one.  The compiler inserts these before its own memory instructions
 // but cannot see into an asm statement, so without them the load may take a
-// stale base address or M0.  s_nop 4 gives five.
+// stale base address or M0.  s_nop 4 gives five; NOP = 0 (one) serves the
+// later copies of a batch that share the first one's descriptor.
+template <int NOP = 4>
 __device__ __forceinline__ void dma16_buf(u32x4_t r, uint32_t voff, FA_LDS void* lds_block) {
+  static_assert(NOP == 0 || NOP == 4, "wait states");
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_block);
-  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               : : "v"(voff), "s"(r), "{m0}"(m0) : "memory");
+  if constexpr (NOP == 4)
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 : : "v"(voff), "s"(r), "{m0}"(m0) : "memory");
+  else
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 : : "v"(voff), "s"(r), "{m0}"(m0) : "memory");
 }
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits

@@ -156,7 +156,10 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
     const int rows = t < 0 ? 0 : min(max(kn - t * BN, 0), BN);
     const u32x4_t r = make_rsrc(src + (int64_t)t * BN * D, rows * ROWB);
 #pragma unroll
-    for (int jj = 0; jj < IPW; ++jj) dma16_buf(r, dma_voff[jj], stage + (wave * IPW + jj) * 1024);
+    for (int jj = 0; jj < IPW; ++jj) {
+      if (jj == 0) dma16_buf<4>(r, dma_voff[jj], stage + (wave * IPW + jj) * 1024);
+      else dma16_buf<0>(r, dma_voff[jj], stage + (wave * IPW + jj) * 1024);
+    }
   };
   // Tile t lives in stage t % NSTG of each ring.  Iteration j reads K(j+1)
   // and V(j-1) and copies K(j+KAHEAD) and V(j+VAHEAD) into the stages they

@@ -162,7 +162,10 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
     const int rows = t < 0 ? 0 : min(max(N - t * BN, 0), BN);
     const u32x4_t r = make_rsrc(src + (int64_t)max(t, 0) * BN * D, rows * ROWB);
 #pragma unroll
-    for (int jj = 0; jj < IPW; ++jj) dma16_buf(r, voff[jj], stage + (wave * IPW + jj) * 1024);
+    for (int jj = 0; jj < IPW; ++jj) {
+      if (jj == 0) dma16_buf<4>(r, voff[jj], stage + (wave * IPW + jj) * 1024);
+      else dma16_buf<0>(r, voff[jj], stage + (wave * IPW + jj) * 1024);
+    }
   };
   // Tile t lives in stage t % NSTG; st = the stage of tile j, carried by the
   // loops.  Iteration j reads K(j+1) and V(j-1).
