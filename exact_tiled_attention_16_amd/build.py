@@ -33,6 +33,13 @@ SOURCES = ["fa_api.cpp", "fwd.hip", "bwd.hip", "quant.hip", "fwd_fp8.hip", "merg
 # Sources whose kernels copy tiles with inline-asm LDS-DMA loads: their device
 # assembly is checked for the wait states those copies need (asmcheck.py).
 DMA_SOURCES = ["fwd.hip", "bwd.hip", "fwd_fp8.hip"]
+# Per-source flags.  The fp8 forward interleaves the P V products of tile j-1
+# with the softmax of tile j step by step; machine sinking moves those
+# products past the rare-path branch at the end of the tile (their first use
+# there is the conditional rescale of O), so that they run back to back with
+# no vector work beside them, and raises register pressure (d = 256 then
+# spills).
+SOURCE_FLAGS = {"fwd_fp8.hip": ["-mllvm", "-disable-machine-sink"]}
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",
@@ -57,7 +64,7 @@ def _hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *COMMON_FLAGS, "-x", "hip", "-c",
+    cmd = [_hipcc(), *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), "-x", "hip", "-c",
            os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -77,8 +84,8 @@ def _check_asm(src: str, verbose: bool) -> int:
     returns the number of copies."""
     from exact_tiled_attention_16_amd import asmcheck
     asm = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".s")
-    cmd = [_hipcc(), *COMMON_FLAGS, "--cuda-device-only", "-S", "-x", "hip",
-           os.path.join(CSRC, src), "-o", asm]
+    cmd = [_hipcc(), *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), "--cuda-device-only", "-S",
+           "-x", "hip", os.path.join(CSRC, src), "-o", asm]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -24,9 +24,9 @@
 //     (power-of-two block scales, or one scale per tensor) has that factor
 //     applied as the e4m3 operand's block-scale exponent of its P V products
 //     (the scaled matrix instruction's E8M0 scale: exact, no vector work);
-//     any other block scale re-expresses O by vs_acc / vs_new under the
-//     matrix products of the iteration before, and a reference raise
-//     rescales O at the end of a tile;
+//     any other block scale re-expresses O by vs_acc / vs_new at the end of
+//     the tile before the block's first P V product, where a reference raise
+//     also rescales O;
 //   * V8 stays row-major in LDS and is read transposed with ds_read_b64_tr_b8
 //     (inside a 16-lane group, lane j's byte e is byte j%8 of the chunk
 //     addressed by lane 2e + j/8); 16-byte chunks of a V row are XOR-swizzled
@@ -308,8 +308,8 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   // [0, kLazySum8] (or the row had none), rescaling O (which already holds
   // P(j-1) V(j-1)) and l to the new reference.
   const uint32_t opaque_zero = (uint32_t)(N >> 31);
-  // `extra`: a value-block factor for O still to apply (one wave per SIMD
-  // re-expresses O here rather than under the matrix products), else 1.
+  // `extra`: a value-block factor for O still to apply (a new value block
+  // whose scale is not a power of two times the accumulator's), else 1.
   auto finish_tile = [&](const Scores& s, Probs& pw, float mul, float psum, float extra) {
     float alpha = 1.0f;
     if (wave_any(!(psum <= kLazySum8))) {
@@ -363,10 +363,12 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   float ks_pre = kscale(-1), vs_pre = vscale(-1);
   // VB: tile j starts a value block (j even: 128-row blocks of two 64-key
   // tiles).  Its scale vs_j is carried either by the E8M0 exponent ea_cur of
-  // the P V products of the block (when vs_j = 2^k vs_acc), or, once P(j-1)
-  // V(j-1) has been issued, by re-expressing O in vs_j: O times vs_acc / vs_j
-  // during the last S(j+1) steps, where the matrix work hides the
-  // multiplies, before P(j) V(j) is added in the next iteration.
+  // the P V products of the block (when vs_j = 2^k vs_acc), or by
+  // re-expressing O in vs_j at the end of the iteration, once P(j-1) V(j-1)
+  // is in O and before P(j) V(j) is added in the next one: O times
+  // vs_acc / vs_j on the rare path of the tile's end, so that the steps
+  // themselves hold no branch (a branch there lets the compiler move the
+  // products and the softmax apart).
   int ea_cur = 127;  // E8M0 exponent of the value block of the P V products
   auto issue_iter = [&](int j, int st) {
     issue(K, j + 3, lds + st * TILEB, koff_dma);
@@ -458,18 +460,6 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
           p_cur[w] = pack4(p[0], p[1], p[2], p[3], p_cur[w]);
         }
       }
-      if constexpr (VB && OCC > 1) {
-        // The last half of the steps: O blocks 2 (step - NSTEP/2) .. +1,
-        // whose products were issued at least NSTEP/2 steps earlier (skipped,
-        // wave-uniformly, when the exponent carries the block scale).
-        if (step >= NSTEP / 2 && vratio != 1.0f) {
-          constexpr int PER = NDB / (NSTEP - NSTEP / 2);
-#pragma unroll
-          for (int i = 0; i < PER; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[(step - NSTEP / 2) * PER + i][r] *= vratio;
-        }
-      }
       if constexpr (DS && DP && DPV && OCC > 1) {
         if (step == 0) __builtin_amdgcn_s_setprio(1);
         if (step == NSTEP / 2) __builtin_amdgcn_s_setprio(0);
@@ -490,7 +480,7 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
             if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s_nxt[kb][r] = -INFINITY;
       }
     }
-    if constexpr (DP) finish_tile(s_cur, p_cur, mul, ps0 + ps1, OCC > 1 ? 1.0f : vratio);
+    if constexpr (DP) finish_tile(s_cur, p_cur, mul, ps0 + ps1, vratio);
     if constexpr (!GROUPED)
       dma_sync<2 * IPW>();
     else if constexpr (POS == -1 || POS == G - 1)
