@@ -115,7 +115,13 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   const int N = a.N;
 
   // One work unit: query tile qt of head bh.
-  auto unit = [&](const int bh, const int qt) __attribute__((always_inline)) {
+  auto unit = [&](const int bh_in, const int qt_in) __attribute__((always_inline)) {
+  // The unit's indices come out of runtime divisions, which the compiler
+  // does on the vector ALU; taken to scalar registers here, every address
+  // and tile bound derived from them stays on the scalar unit instead of
+  // costing vector instructions (and v_readfirstlane) in every iteration.
+  const int bh = __builtin_amdgcn_readfirstlane(bh_in);
+  const int qt = __builtin_amdgcn_readfirstlane(qt_in);
   // In the persistent loop the lane index passes through an empty asm so
   // that nothing derived from it is hoisted out of the loop over units (it
   // would stay live across units and spill at the register limit).
@@ -426,7 +432,7 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
     constexpr int PF = FA_FP8_PF;
     auto frag = [&](int m) {
       if (m < NS_PV) return ld_v(vs, m);
-      return ld_k(ks, (m - NS_PV) / NDC, (m - NS_PV) % NDC);
+      return ld_k(ks, (m - NS_PV) % NKB, (m - NS_PV) / NKB);
     };
     i32x8_t fr[PF + 1];
 #pragma unroll
@@ -442,7 +448,7 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
           if (m < NS_PV) {
             oacc[m] = mfma_fp8_scale_a(f, pf, oacc[m], ea_pv);
           } else {
-            const int kb = (m - NS_PV) / NDC, dc = (m - NS_PV) % NDC;
+            const int kb = (m - NS_PV) % NKB, dc = (m - NS_PV) / NKB;
             s_nxt[kb] = mfma_fp8(f, qf[dc], s_nxt[kb]);
           }
         }
