@@ -34,13 +34,6 @@ pages give no construction, so this module takes the plainest one:
     outlier inputs this changes the attention output's RMSE by +0.1 % (V
     alone: +2 %), since e4m3's relative precision does not depend on where a
     block's values sit inside [2^-6, 448].
-  * A pre-multiplier (``pre_mul``) scales x' in fp32 before the block maxima
-    are taken and divides the stored scale, so dequantised values keep their
-    meaning while the codes see x' * pre_mul.  With power-of-two block
-    scales for Q and K and Q's pre_mul equal to the softmax scale times
-    log2(e), q_scale * k_scale * scale * log2(e) is a power of two up to the
-    fp32 rounding of the stored scale, which the fp8 forward can apply as an
-    exact exponent of its score products.
   * The fp8 attention result is exact attention on the dequantised values
     (code value times stored scale); the device additionally rounds the
     probabilities to e4m3, which the tests bound separately.
@@ -176,30 +169,21 @@ def pow2_ceil(s):
 
 
 def quantize_fp8(x, signs=None, scale_mul: float = 1.0,
-                 per_tensor: bool = False, block: int = 128, pow2: bool = False,
-                 pre_mul: float = 1.0):
+                 per_tensor: bool = False, block: int = 128, pow2: bool = False):
     """Block (or per-tensor) e4m3 quantisation of a [B, H, N, d] tensor.
 
     ``x`` holds the values the device reads (bf16/fp16 widened, exact in fp32).
     ``signs`` (length d, +-1) turns on the rotation x' = H_d(s o x).
-    ``pre_mul`` multiplies x' (fp32) before the block maxima are taken; the
-    stored scale is divided by it, so code * stored still approximates
-    x' * scale_mul.
     ``pow2`` rounds each block scale up to a power of two (block mode only).
-    Returns codes uint8 [B,H,N,d] and scales float32 [B,H,ceil(N/block)].
-    With y = x' * pre_mul, scale =
-    amax(|y|)/448 (``pow2``: rounded up to a power of two), code =
-    e4m3(y / scale) and stored = (scale * scale_mul) / pre_mul, every
-    operation in fp32 in that order.
+    Returns (codes uint8 [B,H,N,d], scales float32 [B,H,ceil(N/block)]); the
+    stored scale is (amax/448) * scale_mul, both operations in fp32 (with
+    ``pow2``: pow2_ceil(amax/448) * scale_mul).
     """
     if pow2 and per_tensor:
         raise ValueError("power-of-two scales are a block-mode option")
-    if not (np.isfinite(pre_mul) and pre_mul > 0):
-        raise ValueError("pre_mul must be positive and finite")
     x = np.asarray(x, dtype=np.float32)
     if signs is not None:
         x = fwht_f32(x * np.asarray(signs, dtype=np.float32))
-    x = (x * np.float32(pre_mul)).astype(np.float32)
     B, H, N, d = x.shape
     nblk = -(-N // block)
     pad = nblk * block - N
@@ -217,7 +201,6 @@ def quantize_fp8(x, signs=None, scale_mul: float = 1.0,
     rows_scale = np.repeat(scale, block, axis=2)[:, :, :N, None]
     codes = e4m3_encode((x / rows_scale).astype(np.float32))
     stored = (scale * np.float32(scale_mul)).astype(np.float32)
-    stored = (stored / np.float32(pre_mul)).astype(np.float32)
     return codes, stored
 
 

@@ -481,60 +481,3 @@ def test_p_rounding_bound_with_score_errors():
         delta = score_error_bound(q, k, causal=causal, scale=scale)
         bound = p_rounding_bound(q, k, vd, causal=causal, scale=scale, score_error=delta)
         assert np.all(np.abs(sim - exact[0, 0]) <= bound[0, 0])
-
-
-def test_pre_mul_power_of_two_changes_nothing():
-    """With power-of-two block scales a pre-multiplier 2^k moves the scale by
-    2^k exactly: codes and stored scales are those of pre_mul = 1."""
-    from exact_tiled_attention_16_amd import inputs
-    q = inputs.qkv_outliers(1, 2, 300, 128, 51)[0].astype(np.float32)
-    s = inputs.signs(128, 51)
-    c0, s0 = quantize_fp8(q, signs=s, scale_mul=1.0 / 128, pow2=True)
-    for k in (-5, 3, 11):
-        c1, s1 = quantize_fp8(q, signs=s, scale_mul=1.0 / 128, pow2=True, pre_mul=2.0 ** k)
-        assert np.array_equal(c0, c1)
-        assert np.array_equal(s0.view(np.uint32), s1.view(np.uint32))
-
-
-@pytest.mark.parametrize("pow2", [False, True])
-def test_pre_mul_keeps_the_dequantised_values(pow2):
-    """code * stored approximates x' * scale_mul within half an e4m3 spacing
-    of the scaled value (relative 2^-4 in the normal range, 2^-10 * scale
-    below it), whatever the pre-multiplier; and the codes are those of the
-    pre-multiplied tensor quantised directly."""
-    from exact_tiled_attention_16_amd import inputs
-    q = inputs.qkv_outliers(1, 2, 300, 64, 52)[0].astype(np.float32)
-    s = inputs.signs(64, 52)
-    pm = float(np.float32(math.log2(math.e) / 8.0))
-    codes, stored = quantize_fp8(q, signs=s, scale_mul=1.0 / 64, pow2=pow2, pre_mul=pm)
-    xr = fwht_f32(q * s.astype(np.float32)).astype(np.float64) / 64
-    deq = dequantize_fp8(codes, stored)
-    sc = np.repeat(stored.astype(np.float64), 128, axis=2)[:, :, :300, None]
-    tol = np.maximum(2.0 ** -4 * np.abs(xr), 2.0 ** -10 * sc) * (1 + 1e-5) + 1e-12
-    assert np.all(np.abs(deq - xr) <= tol)
-    y = (fwht_f32(q * s.astype(np.float32)) * np.float32(pm)).astype(np.float32)
-    c2, _ = quantize_fp8(y, scale_mul=1.0 / 64, pow2=pow2)
-    assert np.array_equal(codes, c2)
-
-
-def test_pre_mul_makes_the_score_multiplier_a_power_of_two():
-    """Q with power-of-two scales and pre_mul = scale * log2(e), K with
-    power-of-two scales: q_scale * k_scale * scale * log2(e) (fp32, as the
-    kernel forms it) lies within 2^-22 of a power of two for every pair of
-    blocks, and not so without the pre-multiplier."""
-    from exact_tiled_attention_16_amd import inputs
-    d = 128
-    q, k, _ = inputs.qkv_outliers(2, 2, 700, d, 53)
-    s = inputs.signs(d, 53)
-    c = np.float32(math.log2(math.e) / math.sqrt(d))
-    _, qs = quantize_fp8(q.astype(np.float32), signs=s, scale_mul=1.0 / d, pow2=True, pre_mul=float(c))
-    _, ks = quantize_fp8(k.astype(np.float32), signs=s, pow2=True)
-    for pre in (True, False):
-        if not pre:
-            _, qs = quantize_fp8(q.astype(np.float32), signs=s, scale_mul=1.0 / d, pow2=True)
-        mul = ((qs * c).astype(np.float32)[..., :, None] * ks[..., None, :]).astype(np.float64)
-        rel = np.abs(mul / np.exp2(np.round(np.log2(mul))) - 1.0)
-        if pre:
-            assert rel.max() <= 2.0 ** -22
-        else:
-            assert rel.max() > 1e-3
