@@ -596,10 +596,17 @@ def config_rows(torch, fa, dev, oracle=True, rounds=3, calls=10, emit=None):
     def randn(*shape):
         return torch.randn(*shape, device=dev, generator=gen).to(torch.bfloat16)
 
-    def timed(call):
-        for _ in range(3):
-            call()
-        torch.cuda.synchronize()
+    def timed(call, warm_s=0.05):
+        # The host oracle between configurations leaves the GPU idle for up
+        # to a second and its clock drops; ~50 ms of the same call first
+        # brings it back, so that every row is the sustained rate.
+        t_end = time.perf_counter() + warm_s
+        while True:
+            for _ in range(3):
+                call()
+            torch.cuda.synchronize()
+            if time.perf_counter() >= t_end:
+                break
         ts = []
         for _ in range(rounds):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
