@@ -164,8 +164,13 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
     koff_dma[jj] = (uint32_t)(r * ROWB + (pc ^ k_swz<D>(r)) * 16);
     voff_dma[jj] = (uint32_t)(r * ROWB + (pc ^ (v_swz<D>(r) >> 1)) * 16);
   }
+  // Rows of tile t: BN up to the last full tile, the remainder on the
+  // partial one, none before the first tile or past the end.  Written as
+  // comparisons and selects, which stay on the scalar unit (a clamp becomes
+  // a vector med3 and a readfirstlane per copy).
+  const int nfull = N / BN, nrem = N % BN;
   auto issue = [&](const uint8_t* src, int t, FA_LDS uint8_t* stage, const uint32_t (&voff)[IPW]) {
-    const int rows = t < 0 ? 0 : min(max(N - t * BN, 0), BN);
+    const int rows = (uint32_t)t < (uint32_t)nfull ? BN : (t == nfull ? nrem : 0);
     const u32x4_t r = make_rsrc(src + (int64_t)max(t, 0) * BN * D, rows * ROWB);
 #pragma unroll
     for (int jj = 0; jj < IPW; ++jj) {
@@ -218,7 +223,9 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
   float m_run = -INFINITY;  // exp2 reference, log2 units
   float l_run = 0.f;
-  float vs_acc = vscale(0);  // V scale the accumulator is expressed in
+  // V scale the accumulator is expressed in, as its fp32 bit pattern: the
+  // comparisons with a new block's scale are integer work on the scalar unit.
+  uint32_t vs_acc = __float_as_uint(vscale(0));
 
   // ---- LDS read offsets.  K rows (A operand of S^T): lane reads row
   // kb*32 + l32, logical chunks 4*dc + 2*hl + {0, 1}.
@@ -234,15 +241,21 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   // row 16 rd + tr_row of the tile and 8-byte unit db*4 + tr_unit.  The
   // swizzle depends on row bits 1 and 3 only, so the four reads rd of one
   // block sit 16 rows apart at one lane-dependent offset: one address per
-  // block, the rest in the instructions' immediate offsets.
+  // block, the rest in the instructions' immediate offsets.  The offsets
+  // include the base of the V stages (NSTG * TILEB), hidden from the
+  // compiler so that it cannot fold it into the immediates: the immediate
+  // field holds 16 bits, enough for a stage offset inside one region but
+  // not for the V region's base on top of it.
   const int tr_e = (lane & 15) >> 1;
   const int tr_unit = ((lane >> 4) & 1) * 2 + (lane & 1);
   int voff[NDB];
   {
     const int row = 8 * (tr_e >> 2) + 4 * hl + (tr_e & 3);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-      voff[db] = row * ROWB + (((db * 4 + tr_unit) ^ v_swz<D>(row)) * 8);
+    for (int db = 0; db < NDB; ++db) {
+      voff[db] = NSTG * TILEB + row * ROWB + (((db * 4 + tr_unit) ^ v_swz<D>(row)) * 8);
+      asm volatile("" : "+v"(voff[db]));
+    }
   }
   auto ld_k = [&](const FA_LDS uint8_t* ks, int kb, int dc) {
     const FA_LDS uint8_t* p = ks + kb * 32 * ROWB;
@@ -293,17 +306,17 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
     return ps0 + ps1;
   };
 
-  // Ratio of two value-block scales, exactly 1 for equal scales, otherwise
-  // by a hardware reciprocal (within 1 ulp; far below the e4m3 rounding of P
-  // and V).
-  auto vscale_ratio = [](float from, float to) {
-    return from == to ? 1.0f : from * __builtin_amdgcn_rcpf(to);
+  // Ratio of two value-block scales (fp32 bit patterns), exactly 1 for
+  // equal scales, otherwise by a hardware reciprocal (within 1 ulp; far below
+  // the e4m3 rounding of P and V).
+  auto vscale_ratio = [](uint32_t from, uint32_t to) {
+    return from == to ? 1.0f : __uint_as_float(from) * __builtin_amdgcn_rcpf(__uint_as_float(to));
   };
-  // E8M0 exponent that carries `to` relative to `from` (127 + the exponent
-  // difference) when both are normal fp32 values with equal mantissas and
-  // the difference fits the E8M0 range; -1 otherwise.
-  auto vscale_exponent = [](float from, float to) {
-    const uint32_t a = __float_as_uint(from), b = __float_as_uint(to);
+  // E8M0 exponent that carries scale `b` relative to scale `a` (fp32 bit
+  // patterns; 127 + the exponent difference) when both are normal values
+  // with equal mantissas and the difference fits the E8M0 range; -1
+  // otherwise.
+  auto vscale_exponent = [](uint32_t a, uint32_t b) {
     const int ea = (int)((a >> 23) & 0xffu), eb = (int)((b >> 23) & 0xffu);
     const int x = 127 + eb - ea;
     const bool ok = ((a ^ b) & 0x807fffffu) == 0 && ea != 0 && eb != 0 && x >= 0 && x <= 254;
@@ -314,9 +327,12 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   // [0, kLazySum8] (or the row had none), rescaling O (which already holds
   // P(j-1) V(j-1)) and l to the new reference.
   const uint32_t opaque_zero = (uint32_t)(N >> 31);
-  // `extra`: a value-block factor for O still to apply (a new value block
-  // whose scale is not a power of two times the accumulator's), else 1.
-  auto finish_tile = [&](const Scores& s, Probs& pw, float mul, float psum, float extra) {
+  // `vchange`: the tile starts a value block whose scale `vto` is not a
+  // power of two times the accumulator's `vfrom` (fp32 bit patterns); O is
+  // then re-expressed by vfrom / vto.  The ratio is formed only on that
+  // rare path.
+  auto finish_tile = [&](const Scores& s, Probs& pw, float mul, float psum, bool vchange,
+                         uint32_t vfrom, uint32_t vto) {
     float alpha = 1.0f;
     if (wave_any(!(psum <= kLazySum8))) {
       asm volatile("" ::: "memory");
@@ -338,8 +354,12 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
       for (int w = 0; w < 8; ++w) pw[w] = (int)((uint32_t)fresh[w] | ((uint32_t)pw[w] & opaque_zero));
     }
     l_run += psum;
-    const float f = alpha * extra;
-    if (f != 1.0f) {  // wave-uniform; rare
+    float f = alpha;
+    if (vchange) {  // wave-uniform; rare
+      asm volatile("" ::: "memory");
+      f *= vscale_ratio(vfrom, vto);
+    }
+    if (f != 1.0f) {  // rare
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int i = 0; i < NDB; ++i)
@@ -381,13 +401,20 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
     issue(V, j + 1, lds + (NSTG + snext(st)) * TILEB, voff_dma);
   };
   auto fused = [&](auto ds_tag, auto ms_tag, auto dp_tag, auto dpv_tag, auto vb_tag, auto pos_tag,
-                   int j, int st, const Scores& s_cur, Scores& s_nxt, Probs& p_cur, const Probs& p_prev) {
+                   auto ph_tag, int j, int st, const Scores& s_cur, Scores& s_nxt, Probs& p_cur,
+                   const Probs& p_prev) {
     constexpr bool DS = decltype(ds_tag)::value, MS = decltype(ms_tag)::value;
     constexpr bool DP = decltype(dp_tag)::value, DPV = decltype(dpv_tag)::value;
     constexpr bool VB = decltype(vb_tag)::value && DP && DPV;
     // POS: -2 / -1 = first / second iteration of the prologue, else the
     // position in a group (0 .. G-1; 0 and 1 with three stages).
     constexpr int POS = decltype(pos_tag)::value;
+    // PH: with eight stages, the parity of the group (j = 1 + G * PH + POS
+    // modulo NSTG) when the caller knows it, else -1.  A known phase makes
+    // the stages of the tiles read compile-time constants, so that every
+    // LDS read address is a lane offset plus an immediate.
+    constexpr int PH = decltype(ph_tag)::value;
+    constexpr bool KNOWN = GROUPED && PH >= 0 && POS >= 0;
     const float ks_j = ks_pre, vs_j = vs_pre;
     ks_pre = kscale(j + 1);
     vs_pre = vscale(j + 1);
@@ -397,21 +424,21 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
       issue_range(2, 0);
     else if constexpr (POS == 0)
       issue_range(j + G + 1, j + G - 1);
-    const FA_LDS uint8_t* ks = lds + (GROUPED ? (j + 1) & MSK : snext(st)) * TILEB;
-    const FA_LDS uint8_t* vs = lds + (NSTG + (GROUPED ? (j - 1) & MSK : sprev(st))) * TILEB;
+    const int kst = KNOWN ? (2 + G * PH + POS) & MSK : GROUPED ? (j + 1) & MSK : snext(st);
+    const int vst = KNOWN ? (G * PH + POS) & MSK : GROUPED ? (j - 1) & MSK : sprev(st);
+    const FA_LDS uint8_t* ks = lds + kst * TILEB;
+    const FA_LDS uint8_t* vs = lds + vst * TILEB;  // voff holds the V region's base
     const float mul = qmul * ks_j;  // tile j's scores to log2 units
     const float m_neg = -m_run;
     const int ea_pv = ea_cur;  // P(j-1) V(j-1): the previous tile's block
-    float vratio = 1.0f;
+    bool vchange = false;
+    const uint32_t vfrom = vs_acc;
     if constexpr (VB) {
-      const int x = vscale_exponent(vs_acc, vs_j);
-      if (x >= 0) {
-        ea_cur = x;
-      } else {
-        vratio = vscale_ratio(vs_acc, vs_j);
-        vs_acc = vs_j;
-        ea_cur = 127;
-      }
+      const uint32_t vb = __float_as_uint(vs_j);
+      const int x = vscale_exponent(vs_acc, vb);
+      vchange = x < 0;
+      ea_cur = vchange ? 127 : x;
+      vs_acc = vchange ? vb : vs_acc;
     }
     if constexpr (DS) {
 #pragma unroll
@@ -486,7 +513,7 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
             if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s_nxt[kb][r] = -INFINITY;
       }
     }
-    if constexpr (DP) finish_tile(s_cur, p_cur, mul, ps0 + ps1, vratio);
+    if constexpr (DP) finish_tile(s_cur, p_cur, mul, ps0 + ps1, vchange, vfrom, vs_acc);
     if constexpr (!GROUPED)
       dma_sync<2 * IPW>();
     else if constexpr (POS == -1 || POS == G - 1)
@@ -516,45 +543,56 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   using P1 = std::integral_constant<int, 1>;
   using P2 = std::integral_constant<int, 2>;
   using P3 = std::integral_constant<int, 3>;
-  fused(T_{}, T_{}, F_{}, F_{}, F_{}, PM2{}, -1, NSTG - 1, sB, sA, pB, pA);  // S(0) -> sA
-  fused(T_{}, T_{}, T_{}, F_{}, F_{}, PM1{}, 0, 0, sA, sB, pA, pB);  // S(1) -> sB, P(0) -> pA
+  using PHR = std::integral_constant<int, -1>;  // group phase known at run time only
+  using PH0 = std::integral_constant<int, 0>;
+  using PH1 = std::integral_constant<int, 1>;
+  fused(T_{}, T_{}, F_{}, F_{}, F_{}, PM2{}, PHR{}, -1, NSTG - 1, sB, sA, pB, pA);  // S(0) -> sA
+  fused(T_{}, T_{}, T_{}, F_{}, F_{}, PM1{}, PHR{}, 0, 0, sA, sB, pA, pB);  // S(1) -> sB, P(0) -> pA
   int j = 1, st = 1;
   // j is odd at the start of a trip; even iterations start a value block.
   if constexpr (NSTG == 3) {
     for (; j + 2 < t_mask; j += 2) {
       const int stb = snext(st);
-      fused(T_{}, F_{}, T_{}, T_{}, F_{}, P0{}, j, st, sB, sA, pB, pA);
-      fused(T_{}, F_{}, T_{}, T_{}, T_{}, P1{}, j + 1, stb, sA, sB, pA, pB);
+      fused(T_{}, F_{}, T_{}, T_{}, F_{}, P0{}, PHR{}, j, st, sB, sA, pB, pA);
+      fused(T_{}, F_{}, T_{}, T_{}, T_{}, P1{}, PHR{}, j + 1, stb, sA, sB, pA, pB);
       st = snext(stb);
     }
     for (; j <= ntiles; j += 2) {
       const int stb = snext(st);
-      fused(T_{}, T_{}, T_{}, T_{}, F_{}, P0{}, j, st, sB, sA, pB, pA);
+      fused(T_{}, T_{}, T_{}, T_{}, F_{}, P0{}, PHR{}, j, st, sB, sA, pB, pA);
       if (j + 1 > ntiles) break;
-      fused(T_{}, T_{}, T_{}, T_{}, T_{}, P1{}, j + 1, stb, sA, sB, pA, pB);
+      fused(T_{}, T_{}, T_{}, T_{}, T_{}, P1{}, PHR{}, j + 1, stb, sA, sB, pA, pB);
       st = snext(stb);
     }
   } else {
-    for (; j + 4 < t_mask; j += 4) {
-      fused(T_{}, F_{}, T_{}, T_{}, F_{}, P0{}, j, 0, sB, sA, pB, pA);
-      fused(T_{}, F_{}, T_{}, T_{}, T_{}, P1{}, j + 1, 0, sA, sB, pA, pB);
-      fused(T_{}, F_{}, T_{}, T_{}, F_{}, P2{}, j + 2, 0, sB, sA, pB, pA);
-      fused(T_{}, F_{}, T_{}, T_{}, T_{}, P3{}, j + 3, 0, sA, sB, pA, pB);
+    // Two groups per trip: the first starts at j = 1 modulo NSTG, so both
+    // groups' stages are compile-time constants.  What is left (at most a
+    // group without masks, then the masked tail) takes the stages from j.
+    static_assert(G == 4 && NSTG == 2 * G, "four iterations per group, two groups per ring");
+    auto group = [&](auto ph, int jg) __attribute__((always_inline)) {
+      fused(T_{}, F_{}, T_{}, T_{}, F_{}, P0{}, ph, jg, 0, sB, sA, pB, pA);
+      fused(T_{}, F_{}, T_{}, T_{}, T_{}, P1{}, ph, jg + 1, 0, sA, sB, pA, pB);
+      fused(T_{}, F_{}, T_{}, T_{}, F_{}, P2{}, ph, jg + 2, 0, sB, sA, pB, pA);
+      fused(T_{}, F_{}, T_{}, T_{}, T_{}, P3{}, ph, jg + 3, 0, sA, sB, pA, pB);
+    };
+    for (; j + 2 * G < t_mask; j += 2 * G) {
+      group(PH0{}, j);
+      group(PH1{}, j + G);
     }
     for (; j <= ntiles; j += 4) {
-      fused(T_{}, T_{}, T_{}, T_{}, F_{}, P0{}, j, 0, sB, sA, pB, pA);
+      fused(T_{}, T_{}, T_{}, T_{}, F_{}, P0{}, PHR{}, j, 0, sB, sA, pB, pA);
       if (j + 1 > ntiles) break;
-      fused(T_{}, T_{}, T_{}, T_{}, T_{}, P1{}, j + 1, 0, sA, sB, pA, pB);
+      fused(T_{}, T_{}, T_{}, T_{}, T_{}, P1{}, PHR{}, j + 1, 0, sA, sB, pA, pB);
       if (j + 2 > ntiles) break;
-      fused(T_{}, T_{}, T_{}, T_{}, F_{}, P2{}, j + 2, 0, sB, sA, pB, pA);
+      fused(T_{}, T_{}, T_{}, T_{}, F_{}, P2{}, PHR{}, j + 2, 0, sB, sA, pB, pA);
       if (j + 3 > ntiles) break;
-      fused(T_{}, T_{}, T_{}, T_{}, T_{}, P3{}, j + 3, 0, sA, sB, pA, pB);
+      fused(T_{}, T_{}, T_{}, T_{}, T_{}, P3{}, PHR{}, j + 3, 0, sA, sB, pA, pB);
     }
   }
   wait_vmcnt<0>();
 
   const float l_tot = sum_halves(l_run);
-  const float inv = l_tot > 0.f ? vs_acc / l_tot : 0.f;
+  const float inv = l_tot > 0.f ? __uint_as_float(vs_acc) / l_tot : 0.f;
   if (qrow < N) {
     uint16_t* orow = static_cast<uint16_t*>(a.o) + base + (int64_t)qrow * D;
 #pragma unroll
