@@ -396,6 +396,7 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   // themselves hold no branch (a branch there lets the compiler move the
   // products and the softmax apart).
   int ea_cur = 127;  // E8M0 exponent of the value block of the P V products
+  i32x8_t pre_fr[FA_FP8_PF];  // first fragments of the next iteration, read ahead
   auto issue_iter = [&](int j, int st) {
     issue(K, j + 3, lds + st * TILEB, koff_dma);
     issue(V, j + 1, lds + (NSTG + snext(st)) * TILEB, voff_dma);
@@ -415,9 +416,13 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
     // LDS read address is a lane offset plus an immediate.
     constexpr int PH = decltype(ph_tag)::value;
     constexpr bool KNOWN = GROUPED && PH >= 0 && POS >= 0;
+    // Inside a group the next iteration's value tile is already published:
+    // the last step reads its first fragments (PRE: this iteration's were
+    // read so), which the next iteration's first products would otherwise
+    // wait for at its start.
+    constexpr bool PRE = KNOWN && POS > 0 && DPV;
+    constexpr bool NXT = KNOWN && POS < G - 1;
     const float ks_j = ks_pre, vs_j = vs_pre;
-    ks_pre = kscale(j + 1);
-    vs_pre = vscale(j + 1);
     if constexpr (!GROUPED)
       issue_iter(j, st);
     else if constexpr (POS == -2)
@@ -457,13 +462,15 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
     // ahead, into a ring of PF + 1 fragments.
     constexpr int M0 = DPV ? 0 : NS_PV, M1 = DS ? NS_PV + NS_S : NS_PV;
     constexpr int PF = FA_FP8_PF;
+    static_assert(!NXT || PF <= NS_PV, "the fragments read ahead are value fragments");
     auto frag = [&](int m) {
       if (m < NS_PV) return ld_v(vs, m);
       return ld_k(ks, (m - NS_PV) % NKB, (m - NS_PV) / NKB);
     };
     i32x8_t fr[PF + 1];
 #pragma unroll
-    for (int m = M0; m < M1 && m < M0 + PF; ++m) fr[(m - M0) % (PF + 1)] = frag(m);
+    for (int m = M0; m < M1 && m < M0 + PF; ++m)
+      fr[(m - M0) % (PF + 1)] = PRE ? pre_fr[m - M0] : frag(m);
 #pragma unroll
     for (int step = 0; step < NSTEP; ++step) {
 #pragma unroll
@@ -499,6 +506,16 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (NXT) {
+      const FA_LDS uint8_t* vs_n = lds + ((G * PH + POS + 1) & MSK) * TILEB;
+#pragma unroll
+      for (int m = 0; m < PF; ++m) pre_fr[m] = ld_v(vs_n, m);
+    }
+    // The scales of tile j + 1, for the next iteration.  Issued here, after
+    // the last fragment wait: a scalar load in flight turns every wait for
+    // an LDS read into a wait for everything.
+    ks_pre = kscale(j + 1);
+    vs_pre = vscale(j + 1);
     if constexpr (DS && MS) {
       const int t = j + 1;
       int lim = N - t * BN - 4 * hl;
