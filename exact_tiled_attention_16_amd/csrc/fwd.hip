@@ -225,7 +225,10 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
   }
   // V operand of O^T (transposed reads): supplier lane 4e + c4 of each 16-lane
   // group addresses row 16*cc + 4*hl + e (+8 for the second read) and column
-  // group 16*g2 + 4*c4 of the 32-column block db.
+  // group 16*g2 + 4*c4 of the 32-column block db.  The offsets include the
+  // base of the V stages (NSTG * TILEB), hidden from the compiler so that it
+  // is not folded into the reads' 16-bit immediates: with a stage known at
+  // compile time, each read is then a lane offset plus an immediate.
   int voff[NDB][2];
   {
     const int e = (lane & 15) >> 2, c4 = lane & 3, g2 = (lane >> 4) & 1;
@@ -234,8 +237,10 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
       const int r = 4 * hl + e + 8 * hi;  // row within a 16-key chunk; cc adds 16 rows
       const int f = swz<D>(r);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        voff[db][hi] = r * ROWB + 16 * ((4 * db + 2 * g2 + (c4 >> 1)) ^ f) + 8 * (c4 & 1);
+      for (int db = 0; db < NDB; ++db) {
+        voff[db][hi] = NSTG * TILEB + r * ROWB + 16 * ((4 * db + 2 * g2 + (c4 >> 1)) ^ f) + 8 * (c4 & 1);
+        asm volatile("" : "+v"(voff[db][hi]));
+      }
     }
   }
   auto ld_k = [&](const FA_LDS uint8_t* ks, int kb, int dc) {
@@ -375,7 +380,7 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
     else if constexpr (!SECOND)
       issue_pair(j);
     const FA_LDS uint8_t* ks = lds + (PAIR ? (j + 1) & 3 : snext(st)) * TILEB;
-    const FA_LDS uint8_t* vs = lds + (NSTG + (PAIR ? (j + 3) & 3 : sprev(st))) * TILEB;
+    const FA_LDS uint8_t* vs = lds + (PAIR ? (j + 3) & 3 : sprev(st)) * TILEB;  // + NSTG * TILEB in voff
     v8 kfr[PF + 1], vfr[PF + 1];
     // S(j+1) runs key block by key block (kb-major) and P(j) consumes S(j)
     // in the same order, so only about half of each score set is live at once.
@@ -493,11 +498,25 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
   // register sets swap roles instead of being copied; then the masked rest.
   // j is odd in the first iteration of a trip.
   int j = 1, st = 1 % NSTG;
-  for (; j + 2 < t_mask; j += 2) {
-    const int stb = snext(st);
-    fused(T_{}, F_{}, T_{}, T_{}, F_{}, j, st, sB, sA, pB, pA);
-    fused(T_{}, F_{}, T_{}, T_{}, T_{}, j + 1, stb, sA, sB, pA, pB);
-    st = snext(stb);
+  if constexpr (NSTG == 3 && !SPARSE) {
+    // Six iterations per trip: iteration j uses stage j % 3, here a
+    // compile-time constant, so that the LDS reads need no address
+    // arithmetic.  The trip ends with j = 1 (mod 6) and st = 1 again.
+    for (; j + 6 < t_mask; j += 6) {
+      fused(T_{}, F_{}, T_{}, T_{}, F_{}, j, 1, sB, sA, pB, pA);
+      fused(T_{}, F_{}, T_{}, T_{}, T_{}, j + 1, 2, sA, sB, pA, pB);
+      fused(T_{}, F_{}, T_{}, T_{}, F_{}, j + 2, 0, sB, sA, pB, pA);
+      fused(T_{}, F_{}, T_{}, T_{}, T_{}, j + 3, 1, sA, sB, pA, pB);
+      fused(T_{}, F_{}, T_{}, T_{}, F_{}, j + 4, 2, sB, sA, pB, pA);
+      fused(T_{}, F_{}, T_{}, T_{}, T_{}, j + 5, 0, sA, sB, pA, pB);
+    }
+  } else {
+    for (; j + 2 < t_mask; j += 2) {
+      const int stb = snext(st);
+      fused(T_{}, F_{}, T_{}, T_{}, F_{}, j, st, sB, sA, pB, pA);
+      fused(T_{}, F_{}, T_{}, T_{}, T_{}, j + 1, stb, sA, sB, pA, pB);
+      st = snext(stb);
+    }
   }
   for (; j <= ntiles; j += 2) {
     const int stb = snext(st);
