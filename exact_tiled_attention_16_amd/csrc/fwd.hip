@@ -379,8 +379,9 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
       issue_iter(j, st);
     else if constexpr (!SECOND)
       issue_pair(j);
-    const FA_LDS uint8_t* ks = lds + (PAIR ? (j + 1) & 3 : snext(st)) * TILEB;
-    const FA_LDS uint8_t* vs = lds + (PAIR ? (j + 3) & 3 : sprev(st)) * TILEB;  // + NSTG * TILEB in voff
+    // st = j % NSTG (a constant in the unrolled main loops).
+    const FA_LDS uint8_t* ks = lds + (PAIR ? (st + 1) & 3 : snext(st)) * TILEB;
+    const FA_LDS uint8_t* vs = lds + (PAIR ? (st + 3) & 3 : sprev(st)) * TILEB;  // + NSTG * TILEB in voff
     v8 kfr[PF + 1], vfr[PF + 1];
     // S(j+1) runs key block by key block (kb-major) and P(j) consumes S(j)
     // in the same order, so only about half of each score set is live at once.
@@ -509,6 +510,14 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
       fused(T_{}, F_{}, T_{}, T_{}, T_{}, j + 3, 1, sA, sB, pA, pB);
       fused(T_{}, F_{}, T_{}, T_{}, F_{}, j + 4, 2, sB, sA, pB, pA);
       fused(T_{}, F_{}, T_{}, T_{}, T_{}, j + 5, 0, sA, sB, pA, pB);
+    }
+  } else if constexpr (NSTG == 4 && !SPARSE) {
+    // Four stages: four iterations (two pairs) per trip, stages 1, 2, 3, 0.
+    for (; j + 4 < t_mask; j += 4) {
+      fused(T_{}, F_{}, T_{}, T_{}, F_{}, j, 1, sB, sA, pB, pA);
+      fused(T_{}, F_{}, T_{}, T_{}, T_{}, j + 1, 2, sA, sB, pA, pB);
+      fused(T_{}, F_{}, T_{}, T_{}, F_{}, j + 2, 3, sB, sA, pB, pA);
+      fused(T_{}, F_{}, T_{}, T_{}, T_{}, j + 3, 0, sA, sB, pA, pB);
     }
   } else {
     for (; j + 2 < t_mask; j += 2) {
