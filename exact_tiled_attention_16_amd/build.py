@@ -3,7 +3,8 @@
 ``python -m exact_tiled_attention_16_amd.build`` (or ``build()``) compiles
 every translation unit under ``csrc/`` to an object in ``_build/`` at the
 repository root and links ``exact_tiled_attention_16_amd/libfa.so`` (and the
-clock probe used by bench.py, ``libfa_probe.so``).  It always
+clock probe used by bench.py, ``libfa_probe.so``, and the instruction-rate
+probe program ``isa_probe``, a measurement aid).  It always
 recompiles; loading code never builds.  The device assembly of the sources
 with LDS-DMA copies is checked for the copies' wait states (asmcheck.py);
 a copy without them fails the build.
@@ -27,6 +28,10 @@ LIB = os.path.join(PKG, "libfa.so")
 # attention library.
 PROBE_SOURCE = "clock_probe.hip"
 PROBE_LIB = os.path.join(PKG, "libfa_probe.so")
+# Measurement aid: a standalone program timing the instructions the kernels
+# are built from (isa_probe.hip); not part of the library.
+RATE_SOURCE = "isa_probe.hip"
+RATE_EXE = os.path.join(PKG, "isa_probe")
 
 ARCH = "gfx950"
 SOURCES = ["fa_api.cpp", "fwd.hip", "bwd.hip", "quant.hip", "fwd_fp8.hip", "merge.hip"]
@@ -114,13 +119,28 @@ def _link(objs, out, verbose):
     os.replace(tmp, out)
 
 
+def _program(src, out, verbose):
+    tmp = out + ".tmp"
+    cmd = [_hipcc(), *COMMON_FLAGS, "-x", "hip", os.path.join(CSRC, src), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
+                         if "packed-fp32-ops" not in l)
+        raise RuntimeError(f"hipcc failed for {src}:\n{msgs}")
+    os.replace(tmp, out)
+
+
 def build(verbose: bool = False, jobs: int = 8) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         checks = [ex.submit(_check_asm, s, verbose) for s in DMA_SOURCES]
+        rate = ex.submit(_program, RATE_SOURCE, RATE_EXE, verbose)
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + [PROBE_SOURCE]))
         for c in checks:
             c.result()
+        rate.result()
     _link([os.path.join(OBJDIR, os.path.splitext(PROBE_SOURCE)[0] + ".o")], PROBE_LIB, verbose)
     _link(objs[:len(SOURCES)], LIB, verbose)
     return LIB
