@@ -18,6 +18,12 @@ straight-line code, counting an instruction as one wait state and
 inside the five-wait-state window, any scalar write of M0 directly before
 the copy, and any block label inside the window (the copy could then be
 reached from code the walk does not see).
+
+The same listings also tell whether a kernel spills: a kernel whose private
+segment is not empty keeps registers (or a stack) in scratch memory.  The
+attention kernels are sized to fit their register budgets, and one that no
+longer does slows down several-fold in the loops that spill, so a build
+whose kernels use scratch fails as well.
 """
 
 from __future__ import annotations
@@ -97,3 +103,22 @@ def check_text(text: str) -> list:
 
 def copies(text: str) -> int:
     return sum(1 for _, kind, inst in _statements(text) if kind == "inst" and _DMA.match(inst))
+
+
+_KNAME = re.compile(r"^\s*\.name:\s+(\S+)")
+_PRIVATE = re.compile(r"^\s*\.private_segment_fixed_size:\s+(\d+)")
+
+
+def scratch_kernels(text: str) -> list:
+    """(kernel symbol, bytes) for every kernel of the listing's code-object
+    metadata whose private segment (scratch) is not empty."""
+    out, name = [], None
+    for line in text.splitlines():
+        m = _KNAME.match(line)
+        if m:
+            name = m.group(1)
+            continue
+        m = _PRIVATE.match(line)
+        if m and name is not None and int(m.group(1)) > 0:
+            out.append((name, int(m.group(1))))
+    return out

@@ -36,7 +36,8 @@ RATE_EXE = os.path.join(PKG, "isa_probe")
 ARCH = "gfx950"
 SOURCES = ["fa_api.cpp", "fwd.hip", "bwd.hip", "quant.hip", "fwd_fp8.hip", "merge.hip"]
 # Sources whose kernels copy tiles with inline-asm LDS-DMA loads: their device
-# assembly is checked for the wait states those copies need (asmcheck.py).
+# assembly is checked for the wait states those copies need and for kernels
+# that spill registers to scratch (asmcheck.py).
 DMA_SOURCES = ["fwd.hip", "bwd.hip", "fwd_fp8.hip"]
 # Per-source flags.  The fp8 forward interleaves the P V products of tile j-1
 # with the softmax of tile j step by step; machine sinking moves those
@@ -105,6 +106,10 @@ def _check_asm(src: str, verbose: bool) -> int:
     n = asmcheck.copies(text)
     if n == 0:
         raise RuntimeError(f"{src}: no LDS-DMA copies found in the device assembly")
+    spills = asmcheck.scratch_kernels(text)
+    if spills:
+        raise RuntimeError(f"{src}: kernels using scratch (register spills):\n"
+                           + "\n".join(f"{k}: {b} bytes" for k, b in spills))
     return n
 
 

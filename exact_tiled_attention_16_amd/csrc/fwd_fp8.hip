@@ -423,6 +423,10 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
     constexpr bool PRE = KNOWN && POS > 0 && DPV;
     constexpr bool NXT = KNOWN && POS < G - 1;
     const float ks_j = ks_pre, vs_j = vs_pre;
+    if constexpr (!GROUPED) {  // d = 256: loaded ahead of the steps (fewer live registers)
+      ks_pre = kscale(j + 1);
+      vs_pre = vscale(j + 1);
+    }
     if constexpr (!GROUPED)
       issue_iter(j, st);
     else if constexpr (POS == -2)
@@ -514,8 +518,10 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
     // The scales of tile j + 1, for the next iteration.  Issued here, after
     // the last fragment wait: a scalar load in flight turns every wait for
     // an LDS read into a wait for everything.
-    ks_pre = kscale(j + 1);
-    vs_pre = vscale(j + 1);
+    if constexpr (GROUPED) {
+      ks_pre = kscale(j + 1);
+      vs_pre = vscale(j + 1);
+    }
     if constexpr (DS && MS) {
       const int t = j + 1;
       int lim = N - t * BN - 4 * hl;

@@ -51,3 +51,23 @@ def test_comments_and_directives_are_skipped_and_copies_counted():
             "\tbuffer_load_dwordx4 v1, s[4:7], 0 offen\n")
     assert asmcheck.copies(text) == 2
     assert _check(text) == []
+
+
+_META = """amdhsa.kernels:
+  - .agpr_count:     0
+    .name:           _ZN2fa12_GLOBAL__N_110fwd_kernelILi128EEEvv
+    .private_segment_fixed_size: {a}
+    .vgpr_count:     242
+  - .agpr_count:     0
+    .name:           _ZN2fa12_GLOBAL__N_114bwd_kv3_kernelILi128EEEvv
+    .private_segment_fixed_size: {b}
+    .vgpr_count:     179
+"""
+
+
+def test_scratch_kernels_lists_only_kernels_with_a_private_segment():
+    assert asmcheck.scratch_kernels(_META.format(a=0, b=0)) == []
+    assert asmcheck.scratch_kernels(_META.format(a=388, b=0)) == [
+        ("_ZN2fa12_GLOBAL__N_110fwd_kernelILi128EEEvv", 388)]
+    assert [k for k, _ in asmcheck.scratch_kernels(_META.format(a=0, b=24))] == [
+        "_ZN2fa12_GLOBAL__N_114bwd_kv3_kernelILi128EEEvv"]
