@@ -495,7 +495,8 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
   }
   fused(T_{}, T_{}, F_{}, F_{}, F_{}, -1, NSTG - 1, sB, sA, pB, pA);  // S(0) -> sA
   fused(T_{}, T_{}, T_{}, F_{}, T_{}, 0, 0, sA, sB, pA, pB);          // S(1) -> sB, P(0) -> pA
-  // Unmasked iterations two per trip, so that the score and probability
+  // Unmasked iterations an even number per trip (six or four with the
+  // stages as constants, else two), so that the score and probability
   // register sets swap roles instead of being copied; then the masked rest.
   // j is odd in the first iteration of a trip.
   int j = 1, st = 1 % NSTG;
