@@ -50,10 +50,9 @@ __device__ __forceinline__ int swz(int r) {
     return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 
-// Explicit instruction order inside the fused steps for head dimensions up
-// to FA_FWD_SGB_MAXD (see `fused`).
-#ifndef FA_FWD_SGB_MAXD
-#define FA_FWD_SGB_MAXD 128
+// Explicit instruction order inside the fused steps (see `fused`).
+#ifndef FA_FWD_SGB
+#define FA_FWD_SGB 1
 #endif
 #ifndef FA_FWD_INTERLEAVE
 #define FA_FWD_INTERLEAVE 1  // hand-placed instruction order in the main loop
@@ -439,16 +438,27 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
         if (step == 0) __builtin_amdgcn_s_setprio(1);
         if (step == NSTEP / 2) __builtin_amdgcn_s_setprio(0);
       }
-      // Order inside a full step: the score product, four vector
-      // instructions, the P V product, the step's fragment reads, the rest
-      // of the vector work.  The compiler's own order measured 1.6-2.0 %
-      // slower at d = 128 and 0.4 % at d = 64 (nine orders were timed).
-      if constexpr (DS && DP && DPV && QB == 1 && D <= FA_FWD_SGB_MAXD) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // matrix
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // vector
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // matrix
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // vector
+      // Order inside a full step.  d <= 128 (two waves per SIMD): the score
+      // product, four vector instructions, the P V product, the step's
+      // fragment reads, the rest of the vector work; the compiler's own
+      // order measured 1.6-2.0 % slower at d = 128 and 0.4 % at d = 64
+      // (nine orders were timed).  d = 256 (one wave per SIMD, half a
+      // probability pair per step): the score product, the reads, the P V
+      // product, the vector work (1.1 % faster; the d <= 128 order was 7 %
+      // slower there).
+      if constexpr (DS && DP && DPV && QB == 1 && FA_FWD_SGB) {
+        if constexpr (D <= 128) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // matrix
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // vector
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // matrix
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // vector
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // matrix
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // matrix
+          __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // vector
+        }
       }
 #if FA_FWD_INTERLEAVE
       __builtin_amdgcn_sched_barrier(0);

@@ -41,13 +41,9 @@
 #ifndef FA_FP8_PF
 #define FA_FP8_PF 2
 #endif
-// Explicit instruction order inside the fused steps (see `fused`), for head
-// dimensions up to FA_FP8_SGB_MAXD.
+// Explicit instruction order inside the fused steps (see `fused`).
 #ifndef FA_FP8_SGB
 #define FA_FP8_SGB 1
-#endif
-#ifndef FA_FP8_SGB_MAXD
-#define FA_FP8_SGB_MAXD 128
 #endif
 
 namespace fa {
@@ -516,19 +512,21 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
         if (step == 0) __builtin_amdgcn_s_setprio(1);
         if (step == NSTEP / 2) __builtin_amdgcn_s_setprio(0);
       }
-      // Order inside a full step at d <= 128: the first product, the step's
-      // fragment reads, four vector instructions, the second product, the
-      // rest of the vector work.  Left to itself the compiler issues the two
-      // products nearly back to back, and the wave then waits for the matrix
-      // unit before its vector work; this order measured 1.2-1.7 % faster
-      // at d = 128 (other splits of the vector work around the second
-      // product, 0-28 instructions before it, measured in between).
-      if constexpr (DS && DP && DPV && FA_FP8_SGB && D <= FA_FP8_SGB_MAXD) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // matrix
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // vector
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // matrix
-        __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);  // vector
+      // Order inside a full step: the first product, the step's fragment
+      // reads, a few vector instructions (four at d <= 128, two at d = 256),
+      // the second product, the rest of the vector work.  Left to itself the
+      // compiler issues the two products nearly back to back, and the wave
+      // then waits for the matrix unit before its vector work; this order
+      // measured 1.2-1.7 % faster at d = 128 (other splits, 0-28 vector
+      // instructions before the second product, in between) and 5-6 % at
+      // d = 256.
+      if constexpr (DS && DP && DPV && FA_FP8_SGB) {
+        constexpr int kBefore = D == 256 ? 2 : 4;
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // matrix
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);        // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x002, kBefore, 0);  // vector
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // matrix
+        __builtin_amdgcn_sched_group_barrier(0x002, 28 - kBefore, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
