@@ -636,21 +636,43 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
 
   const float l_tot = sum_halves(l_run);
   const float inv = l_tot > 0.f ? __uint_as_float(vs_acc) / l_tot : 0.f;
-  if (qrow < N) {
-    uint16_t* orow = static_cast<uint16_t*>(a.o) + base + (int64_t)qrow * D;
+  // O leaves through LDS: each lane holds one query row in 8-byte pieces, so
+  // storing from the accumulators would scatter every store instruction over
+  // 32 rows (measured ~6,000 cycles per wave).  The wave writes its 32 x D
+  // block into LDS (rows padded by 8 bytes, so the 8-byte writes of one
+  // half-wave hit distinct banks), then stores whole rows, 16 bytes per lane.
+  // The K/V ring is free once every wave has left the loop.
+  constexpr int OROWB = 2 * D + 8;
+  static_assert(NW * 32 * OROWB <= 2 * NSTG * TILEB, "the O blocks fit in the K/V ring");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  FA_LDS uint8_t* ost = lds + wave * 32 * OROWB;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+  for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2_t w;
-        w[0] = Elem<0>::pack2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
-        w[1] = Elem<0>::pack2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2_t*>(orow + db * 32 + 8 * g + 4 * hl) = w;
-      }
+    for (int g = 0; g < 4; ++g) {
+      u32x2_t w;
+      w[0] = Elem<0>::pack2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
+      w[1] = Elem<0>::pack2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+      *reinterpret_cast<FA_LDS u32x2_t*>(ost + l32 * OROWB + 2 * (db * 32 + 8 * g + 4 * hl)) = w;
     }
-    if (hl == 0 && a.lse != nullptr)
-      a.lse[(int64_t)bh * N + qrow] = m_run * kLn2 + __logf(l_tot);
   }
+  asm volatile("" ::: "memory");
+  {
+    constexpr int LPR = D / 8;          // lanes per row, 16 bytes each
+    constexpr int RPI = 64 / LPR;       // rows per store instruction
+    const int r0 = lane / LPR, cb = (lane % LPR) * 16;
+#pragma unroll
+    for (int k = 0; k < 32 / RPI; ++k) {
+      const int r = r0 + RPI * k;
+      const u32x4_t v = ld_lds16(ost + r * OROWB + cb);
+      if (qw0 + r < N)
+        *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(a.o) + 2 * (base + (int64_t)(qw0 + r) * D) +
+                                    cb) = v;
+    }
+  }
+  if (qrow < N && hl == 0 && a.lse != nullptr)
+    a.lse[(int64_t)bh * N + qrow] = m_run * kLn2 + __logf(l_tot);
   };  // unit
 
   if constexpr (PERSIST) {
