@@ -564,13 +564,13 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
   wait_vmcnt<0>();  // copies past the last tile must land before LDS is released
 
   // Epilogue: normalise, round, store; LSE in natural log.
+  if constexpr (PARTIAL) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = qw0 + 32 * qb + l32;
-    const float l_tot = sum_halves(l_run[qb]);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (qrow < N) {
-      if constexpr (PARTIAL) {
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qrow = qw0 + 32 * qb + l32;
+      const float l_tot = sum_halves(l_run[qb]);
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      if (qrow < N) {
         const int64_t slot = ((int64_t)s * a.bh + bh) * N + qrow;
         float* orow = a.o32 + slot * D;
 #pragma unroll
@@ -583,21 +583,50 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
         }
         // No visible key: l = 0, O = 0 and the log-sum-exp is -inf.
         if (hl == 0) a.lse32[slot] = m_run[qb] * kLn2 + __logf(l_tot);
-      } else {
-        uint16_t* orow = static_cast<uint16_t*>(a.o) + base + (int64_t)qrow * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            u32x2_t w;
-            w[0] = E::pack2(oacc[qb][db][4 * g + 0] * inv, oacc[qb][db][4 * g + 1] * inv);
-            w[1] = E::pack2(oacc[qb][db][4 * g + 2] * inv, oacc[qb][db][4 * g + 3] * inv);
-            *reinterpret_cast<u32x2_t*>(orow + db * 32 + 8 * g + 4 * hl) = w;
-          }
-        }
-        if (hl == 0 && a.lse != nullptr)
-          a.lse[(int64_t)bh * N + qrow] = m_run[qb] * kLn2 + __logf(l_tot);
       }
+    }
+  } else {
+    // A lane holds its query row in 8-byte pieces, so stores straight from
+    // the accumulators would scatter each instruction over 32 rows.  Each
+    // wave writes its rows into LDS instead (rows padded by 8 bytes, so the
+    // 8-byte writes of one half-wave hit distinct banks) and stores whole
+    // rows, 16 bytes per lane.  The K/V ring is free once every wave has
+    // left the loop (each wave's own copies have landed, see above).
+    constexpr int OROWB = 2 * D + 8;
+    static_assert(NW * WQ * OROWB <= 2 * NSTG * TILEB, "the O blocks fit in the K/V ring");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    FA_LDS uint8_t* ost = lds + wave * WQ * OROWB;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float l_tot = sum_halves(l_run[qb]);
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2_t w;
+          w[0] = E::pack2(oacc[qb][db][4 * g + 0] * inv, oacc[qb][db][4 * g + 1] * inv);
+          w[1] = E::pack2(oacc[qb][db][4 * g + 2] * inv, oacc[qb][db][4 * g + 3] * inv);
+          *reinterpret_cast<FA_LDS u32x2_t*>(ost + (32 * qb + l32) * OROWB +
+                                             2 * (db * 32 + 8 * g + 4 * hl)) = w;
+        }
+      }
+      const int qrow = qw0 + 32 * qb + l32;
+      if (qrow < N && hl == 0 && a.lse != nullptr)
+        a.lse[(int64_t)bh * N + qrow] = m_run[qb] * kLn2 + __logf(l_tot);
+    }
+    asm volatile("" ::: "memory");
+    constexpr int LPR = D / 8;     // lanes per row, 16 bytes each
+    constexpr int RPI = 64 / LPR;  // rows per store instruction
+    const int r0 = lane / LPR, cb = (lane % LPR) * 16;
+#pragma unroll
+    for (int k = 0; k < WQ / RPI; ++k) {
+      const int r = r0 + RPI * k;
+      const u32x4_t v = ld_lds16(ost + r * OROWB + cb);
+      if (qw0 + r < N)
+        *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(a.o) + 2 * (base + (int64_t)(qw0 + r) * D) +
+                                    cb) = v;
     }
   }
   };  // unit
