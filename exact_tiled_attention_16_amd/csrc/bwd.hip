@@ -44,13 +44,10 @@
 #include "common.h"
 #include "kernels.h"
 
-// LDS fragments read ahead of the matrix products in bwd_kv3_kernel: row
-// reads (S / dP) and transposed reads (dV / dK).
-#ifndef FA_KV2_PF_ROW
-#define FA_KV2_PF_ROW 2
-#endif
-#ifndef FA_KV2_PF_TR
-#define FA_KV2_PF_TR 2
+// LDS fragments read ahead of the matrix products in bwd_kv3_kernel (row
+// and transposed reads alike).
+#ifndef FA_KV_PF
+#define FA_KV_PF 2
 #endif
 
 namespace fa {
@@ -291,54 +288,88 @@ bwd_kv3_kernel(BwdArgs a) {
           for (int t = 0; t < 4; ++t) sacc[qb][4 * g + t] = v[t];
         }
     };
-    // sacc += T K^T or T V^T over the tile's rows T (Q or dO).
-    auto row_products = [&](const FA_LDS uint8_t* src) {
-      constexpr int PF = FA_KV2_PF_ROW, NST = NQB * NDC;
+    // A tile's matrix work is a stream of row products (sacc += T K^T or
+    // T V^T over rows T, block qb = k / NDC) and transposed products (acc +=
+    // T^T W over 16-query chunks cc = k / NDB), NH of each, in the order of
+    // the role (HALVES = 1: the first kind only).  Fragments are read PF
+    // instructions ahead, across the two halves.  After the product of step
+    // m comes vec(m), a share of the vector work, so that a wave forms its
+    // probabilities or dS' words under its own products rather than between
+    // them.
+    constexpr int NH = NQB * NDC;
+    static_assert(NH == NDB * (BQ / 16), "both halves have the same length");
+    auto stream = [&](auto rows_first_tag, auto halves_tag, const FA_LDS uint8_t* rsrc,
+                      const FA_LDS uint8_t* tsrc, auto&& vec) {
+      constexpr bool ROWS_FIRST = decltype(rows_first_tag)::value;
+      constexpr int NM = decltype(halves_tag)::value * NH;
+      constexpr int PF = FA_KV_PF;
+      auto is_row = [](int m) { return ROWS_FIRST ? m < NH : m >= NH; };
+      auto frag = [&](int m) {
+        const int k = m % NH;
+        return is_row(m) ? ld_row(rsrc, k / NDC, k % NDC) : ld_tr(tsrc, k / NDB, k % NDB);
+      };
       v8 fr[PF + 1];
 #pragma unroll
-      for (int s = 0; s < PF; ++s) fr[s] = ld_row(src, s / NDC, s % NDC);
+      for (int m = 0; m < PF; ++m) fr[m] = frag(m);
 #pragma unroll
-      for (int s = 0; s < NST; ++s) {
-        if (s + PF < NST) fr[(s + PF) % (PF + 1)] = ld_row(src, (s + PF) / NDC, (s + PF) % NDC);
-        sacc[s / NDC] = E::mfma(fr[s % (PF + 1)], kvf[s % NDC], sacc[s / NDC]);
+      for (int m = 0; m < NM; ++m) {
+        if (m + PF < NM) fr[(m + PF) % (PF + 1)] = frag(m + PF);
+        const int k = m % NH;
+        if (is_row(m)) {
+          sacc[k / NDC] = E::mfma(fr[m % (PF + 1)], kvf[k % NDC], sacc[k / NDC]);
+        } else {
+          const int cc = k / NDB, db = k % NDB;
+          const uint32_t* w = pw[cc >> 1][cc & 1];
+          acc[db] = E::mfma(fr[m % (PF + 1)], __builtin_bit_cast(v8, u32x4_t{w[0], w[1], w[2], w[3]}),
+                            acc[db]);
+        }
+        vec(m);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    // acc += T^T W over the 64 queries of a tile (T read transposed, W = pw).
-    auto acc_products = [&](const FA_LDS uint8_t* src) {
-      constexpr int PF = FA_KV2_PF_TR, NST = NDB * (BQ / 16);
-      v8 fr[PF + 1];
-#pragma unroll
-      for (int s = 0; s < PF; ++s) fr[s] = ld_tr(src, s / NDB, s % NDB);
-#pragma unroll
-      for (int s = 0; s < NST; ++s) {
-        if (s + PF < NST) fr[(s + PF) % (PF + 1)] = ld_tr(src, (s + PF) / NDB, (s + PF) % NDB);
-        const int cc = s / NDB, db = s % NDB;
-        const uint32_t* w = pw[cc >> 1][cc & 1];
-        acc[db] = E::mfma(fr[s % (PF + 1)], __builtin_bit_cast(v8, u32x4_t{w[0], w[1], w[2], w[3]}),
-                          acc[db]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
+    static_assert(NQB == 2, "two query blocks per tile");
     // Role 1: dS' of the previous tile from its P (buffer pb) and the kept
-    // dP - D, packed into pw; then dK^T += Q^T dS'.
-    auto ds_and_dk = [&](int pb, const FA_LDS uint8_t* qprev) {
+    // dP - D, dK^T += Q^T dS' over that tile's rows qprev, then (DP) dP - D
+    // of the current tile over its dO rows (stage sb).  Block 0's first four
+    // words are formed before the first product (chunk 0 uses them), its
+    // other four under chunk 0's products, block 1's under chunk 1's; then
+    // sacc is free and the row statistics are read, well ahead of the dP
+    // products.  The dS' + dK phase is the critical path of a tile: it runs
+    // at raised priority, so the S side's products fill in around it (2-4 %
+    // faster than equal priorities; raising either role for the whole tile
+    // was slower at d = 128).
+    auto dk_tile = [&](int pb, const FA_LDS uint8_t* qprev, auto dp_tag, const FA_LDS uint8_t* sb) {
+      constexpr bool DP = decltype(dp_tag)::value;
+      u32x4_t pp[NQB][2];
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const u32x4_t pp = *(const FA_LDS u32x4_t*)pchunk(pb, qb * 2 + h);
+        for (int h = 0; h < 2; ++h) pp[qb][h] = *(const FA_LDS u32x4_t*)pchunk(pb, qb * 2 + h);
+      auto dsword = [&](int qb, int x) {
+        // Word x = 4h + w holds registers 8h + 2w, 8h + 2w + 1 of block qb.
+        const int h = x >> 2, w = x & 3, r = 8 * h + 2 * w;
+        const uint32_t word = pp[qb][h][w];
+        const float lo = to_f32<DT>((uint16_t)(word & 0xffffu));
+        const float hi = to_f32<DT>((uint16_t)(word >> 16));
+        pw[qb][h][w] = E::pack2(lo * sacc[qb][r], hi * sacc[qb][r + 1]);
+      };
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            // Word w holds registers 8h + 2w, 8h + 2w + 1 of block qb.
-            const int r = 8 * h + 2 * w;
-            const uint32_t word = pp[w];
-            const float lo = to_f32<DT>((uint16_t)(word & 0xffffu));
-            const float hi = to_f32<DT>((uint16_t)(word >> 16));
-            pw[qb][h][w] = E::pack2(lo * sacc[qb][r], hi * sacc[qb][r + 1]);
-          }
-        }
-      acc_products(qprev);
+      for (int x = 0; x < 4; ++x) dsword(0, x);
+      stream(std::false_type{}, std::integral_constant<int, DP ? 2 : 1>{}, sb + QTB, qprev,
+             [&](int m) {
+#pragma unroll
+               for (int y = 0; y < 4; ++y)
+                 if (m == (y * NDB) / 4) dsword(0, 4 + y);
+#pragma unroll
+               for (int x = 0; x < 8; ++x)
+                 if (m == NDB + (x * NDB) / 8) dsword(1, x);
+               if constexpr (DP) {
+                 if (m == 2 * NDB - 1) load_stats(sb);
+                 if (m == NH - 1) __builtin_amdgcn_s_setprio(0);
+               }
+             });
+      if constexpr (!DP) __builtin_amdgcn_s_setprio(0);
     };
 
     auto iteration = [&](auto m_tag, auto first_tag, int i, int st) {
@@ -348,38 +379,40 @@ bwd_kv3_kernel(BwdArgs a) {
       const int q0 = i * BQ;
       issue_tile(i + 1, st == 2 ? 0 : st + 1);  // the stage of tile i-2
       if constexpr (ROLE == 0) {
-        load_stats(sb);
-        row_products(sb);  // S(i) - LSE/scale
+        // S(i) over Q rows (block 0, then block 1), then dV^T += dO(i)^T P(i)
+        // (chunks 0-1 use block 0's P, 2-3 block 1's).  Block 0's P words
+        // are formed under block 1's S products, block 1's under the first
+        // half of the dV products; each 16-byte P chunk goes to LDS once
+        // complete.
         const float c = a.scale_log2;
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              const int r = 8 * h + 2 * w;
-              float p0 = fast_exp2(sacc[qb][r] * c), p1 = fast_exp2(sacc[qb][r + 1] * c);
-              if constexpr (MASKED) {
-                const int q = q0 + qb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-                if (key > q) p0 = 0.f;
-                if (key > q + 1) p1 = 0.f;
-              }
-              pw[qb][h][w] = E::pack2(p0, p1);
-            }
+        auto pword = [&](int qb, int x) {
+          const int h = x >> 2, w = x & 3, r = 8 * h + 2 * w;
+          float p0 = fast_exp2(sacc[qb][r] * c), p1 = fast_exp2(sacc[qb][r + 1] * c);
+          if constexpr (MASKED) {
+            const int q = q0 + qb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+            if (key > q) p0 = 0.f;
+            if (key > q + 1) p1 = 0.f;
+          }
+          pw[qb][h][w] = E::pack2(p0, p1);
+          if (w == 3)
             *(FA_LDS u32x4_t*)pchunk(i & 1, qb * 2 + h) =
                 u32x4_t{pw[qb][h][0], pw[qb][h][1], pw[qb][h][2], pw[qb][h][3]};
-          }
-        acc_products(sb + QTB);  // dV^T += dO(i)^T P(i)
-      } else {
-        // The dS' + dK phase is the critical path of a tile: it runs at raised
-        // priority, so the S side's products fill in around it (2-4 % faster
-        // than equal priorities; raising either role for the whole tile was
-        // slower at d = 128).
-        __builtin_amdgcn_s_setprio(1);
-        if constexpr (!FIRST) ds_and_dk((i - 1) & 1, lds + (st == 0 ? 2 : st - 1) * STAGEB);
-        __builtin_amdgcn_s_setprio(0);
+        };
         load_stats(sb);
-        row_products(sb + QTB);  // dP(i) - D, kept for the next tile
+        stream(std::true_type{}, std::integral_constant<int, 2>{}, sb, sb + QTB, [&](int m) {
+          constexpr int H2 = NH / 2;
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            if (m == H2 + (x * H2) / 8) pword(0, x);
+            if (m == NH + (x * H2) / 8) pword(1, x);
+          }
+        });
+      } else if constexpr (FIRST) {
+        // dP(i) - D only.
+        load_stats(sb);
+        stream(std::true_type{}, std::integral_constant<int, 1>{}, sb + QTB, sb, [](int) {});
+      } else {
+        dk_tile((i - 1) & 1, lds + (st == 0 ? 2 : st - 1) * STAGEB, std::true_type{}, sb);
       }
       tile_sync();  // P(i) published; tile i+1 landed
     };
@@ -405,7 +438,8 @@ bwd_kv3_kernel(BwdArgs a) {
         st = st == 2 ? 0 : st + 1;
       }
       // Role 1: dK of the last tile (its P was published by the last barrier).
-      if constexpr (ROLE == 1) ds_and_dk((nq - 1) & 1, lds + (st == 0 ? 2 : st - 1) * STAGEB);
+      if constexpr (ROLE == 1)
+        dk_tile((nq - 1) & 1, lds + (st == 0 ? 2 : st - 1) * STAGEB, std::false_type{}, lds);
     }
     wait_vmcnt<0>();  // copies past the last tile must land before LDS is released
 
