@@ -92,14 +92,30 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
   constexpr int NDB = D / 32;
   constexpr int NDC = D / 16;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NSTG * TILEB];
+  // The non-causal persistent grid (PERSIST && !CAUSAL) copies the next
+  // unit's first two K tiles into stages 0 and 1 while the current unit's O
+  // passes through LDS: O is then staged above them.
+  constexpr bool PREFETCH = PERSIST && !CAUSAL;
+  constexpr int OROWB = 2 * D + 8;  // bytes per staged O row (8 bytes of padding)
+  constexpr int OSTB = PREFETCH ? 2 * TILEB : 0;
+  constexpr int SMEM = 2 * NSTG * TILEB > OSTB + NW * WQ * OROWB ? 2 * NSTG * TILEB
+                                                                 : OSTB + NW * WQ * OROWB;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
   FA_LDS uint8_t* lds = (FA_LDS uint8_t*)smem;  // K stage s at s*TILEB, V at (NSTG+s)*TILEB
 
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave-uniform (scalar)
   const int N = a.N;
 
+  // Q^T operand of block qb: lane holds query qw0 + 32 qb + l32, head-dim
+  // slots dc*16 + 8*hl + [0, 8).  Declared outside the unit: the persistent
+  // grid loads the next unit's rows here during the current unit's epilogue.
+  v8 qf[QB][NDC];
+
   // One work unit: query tile qt of head bh against the keys of split s.
-  auto unit = [&](const int bh, const int qt, const int s) {
+  // nxt: the next unit of this workgroup (persistent non-causal grid), else
+  // -1; pre: this unit's Q rows and first two K tiles were fetched by the
+  // previous unit's epilogue.
+  auto unit = [&](const int bh, const int qt, const int s, const int nxt, const bool pre) {
   // The lane index passes through an empty asm so that nothing derived from
   // it is hoisted out of a loop over units (it would stay live across units
   // and spill at the register limit).
@@ -193,19 +209,19 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
     issue(V, j + 2, lds + (NSTG + ((j + 2) & 3)) * TILEB);
   };
 
-  // Q^T operand of block qb: lane holds query qw0 + 32 qb + l32, head-dim
-  // slots dc*16 + 8*hl + [0, 8).
-  v8 qf[QB][NDC];
+  auto load_q = [&](const uint16_t* Qh, int qw) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = qw0 + 32 * qb + l32;
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qrow = qw + 32 * qb + l32;
 #pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) {
-      u32x4_t raw = {0u, 0u, 0u, 0u};
-      if (qrow < N) raw = ld_global16(Q + (int64_t)qrow * D + dc * 16 + 8 * hl);
-      qf[qb][dc] = __builtin_bit_cast(v8, raw);
+      for (int dc = 0; dc < NDC; ++dc) {
+        u32x4_t raw = {0u, 0u, 0u, 0u};
+        if (qrow < N) raw = ld_global16(Qh + (int64_t)qrow * D + dc * 16 + 8 * hl);
+        qf[qb][dc] = __builtin_bit_cast(v8, raw);
+      }
     }
-  }
+  };
+  if (!pre) load_q(Q, qw0);
 
   f32x16_t oacc[QB][NDB];
   float m_run[QB], l_run[QB];  // exp2 reference (log2 units), this lane's share of l
@@ -512,10 +528,15 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
   // leaves exactly those in flight, so K(1) has landed for iteration 0.
   // Four stages: the prologue pair (-1, 0) reads K(0) and K(1), copied and
   // published first.
-  issue(K, 0, lds);
+  if (!pre) {
+    issue(K, 0, lds);
+    if constexpr (NSTG >= 3) issue(K, 1, lds + TILEB);
+  }
   if constexpr (NSTG >= 3) {
-    issue(K, 1, lds + TILEB);
-    dma_sync<PAIR ? 0 : IPW>();
+    if (pre)
+      dma_sync<0>();
+    else
+      dma_sync<PAIR ? 0 : IPW>();
   } else {
     dma_sync<0>();
   }
@@ -592,11 +613,20 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
     // 8-byte writes of one half-wave hit distinct banks) and stores whole
     // rows, 16 bytes per lane.  The K/V ring is free once every wave has
     // left the loop (each wave's own copies have landed, see above).
-    constexpr int OROWB = 2 * D + 8;
-    static_assert(NW * WQ * OROWB <= 2 * NSTG * TILEB, "the O blocks fit in the K/V ring");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    FA_LDS uint8_t* ost = lds + wave * WQ * OROWB;
+    if constexpr (PREFETCH) {
+      // The next unit's Q rows (this unit's are dead) and its first two K
+      // tiles, into the stages below the O blocks, in flight while O leaves.
+      if (nxt >= 0) {
+        const int nbh = nxt / a.n_qtiles, nqt = nxt % a.n_qtiles;
+        load_q(static_cast<const uint16_t*>(a.q) + (int64_t)nbh * N * D, nqt * BM + wave * WQ);
+        const uint16_t* Kn = static_cast<const uint16_t*>(a.k) + ((int64_t)nbh * a.Nk + kb0) * D;
+        issue(Kn, 0, lds);
+        issue(Kn, 1, lds + TILEB);
+      }
+    }
+    FA_LDS uint8_t* ost = lds + OSTB + wave * WQ * OROWB;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float l_tot = sum_halves(l_run[qb]);
@@ -631,15 +661,33 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
   }
   };  // unit
 
-  if constexpr (PERSIST) {
+  if constexpr (PERSIST && CAUSAL) {
     // A causal query tile qt costs qt + 1 key tiles: rank 0 is the last one.
     lpt_units(a.n_qtiles, a.bh, a.pin != 0, [&](int bh, int rank) {
-      unit(bh, a.n_qtiles - 1 - rank, 0);
+      unit(bh, a.n_qtiles - 1 - rank, 0, -1, false);
       // The next unit's first copies reuse the ring: every wave must be done
       // reading it (this wave's own copies have all landed already).
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     });
+  } else if constexpr (PERSIST) {
+    // Non-causal, all units alike: workgroup w takes units w, w + G, ... of
+    // the (head, query tile) order under the XCD remap of the one-unit grid
+    // below (G is a multiple of 8, so each stays on the XCD it had there),
+    // and fetches each next unit's Q rows and first K tiles during the
+    // current unit's epilogue.
+    static_assert(!PARTIAL && !SPARSE && NSTG >= 3, "plain non-causal forward");
+    const int total = a.n_qtiles * a.bh;
+    for (int u = blockIdx.x; u < total; u += gridDim.x) {
+      const int logical = xcd_remap(u, total);
+      const int nu = u + (int)gridDim.x;
+      unit(logical / a.n_qtiles, logical % a.n_qtiles, 0, nu < total ? xcd_remap(nu, total) : -1,
+           u != (int)blockIdx.x);
+      // The next unit's copies and O blocks reuse the ring: every wave must
+      // be done reading it.
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
   } else {
     // Units in (head, split, query tile) order: the query tiles of one split
     // read the same keys, and the XCD remap keeps them on one L2.
@@ -647,7 +695,7 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
     const int hs = logical / a.n_qtiles;
     int qt = logical % a.n_qtiles;
     if (CAUSAL) qt = a.n_qtiles - 1 - qt;  // longest key ranges first
-    unit(hs / a.n_split, qt, hs % a.n_split);
+    unit(hs / a.n_split, qt, hs % a.n_split, -1, false);
   }
 }
 
@@ -726,7 +774,7 @@ hipError_t launch_one(const FwdArgs& a, int BH, hipStream_t stream,
 // first.  Both produce bit-identical outputs.
 template <int D, int DT>
 hipError_t launch_causal(const FwdArgs& a, int BH, bool causal, bool per_tile, hipStream_t s) {
-  if (!causal) return launch_one<D, false, false, false, DT>(a, BH, s);
+  if (!causal) return launch_one<D, false, true, false, DT>(a, BH, s);
   if (per_tile) return launch_one<D, true, false, false, DT>(a, BH, s);
   return launch_one<D, true, true, false, DT>(a, BH, s);
 }
