@@ -782,7 +782,7 @@ hipError_t launch_grid(BwdArgs a, int BH, bool causal, int threads, hipStream_t 
     hipLaunchKernelGGL(KPlain, dim3((unsigned)units), dim3(threads), 0, s, a);
     return hipGetLastError();
   }
-  const int slots = resident_slots(KPersist, threads);
+  const int slots = resident_slots<KPersist>(threads);
   if (slots <= 0) return hipErrorInvalidValue;
   const int64_t grid = std::min<int64_t>(units, slots);
   a.pin = (BH % 8 == 0 && grid % 8 == 0) ? 1 : 0;

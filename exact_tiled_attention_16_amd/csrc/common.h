@@ -214,10 +214,12 @@ __device__ __forceinline__ void lpt_units(int ntiles, int nheads, bool pin, F&& 
   }
 }
 
-// Workgroups of `kernel` (with `threads` threads) resident at once on the
-// current device, cached per device and kernel; 0 if it cannot be queried.
-template <typename K>
-int resident_slots(K kernel, int threads) {
+// Workgroups of `Kernel` (with `threads` threads) resident at once on the
+// current device, cached per device and kernel (the kernel is a template
+// argument, so each instantiation has its own cache: kernels of one
+// signature may differ in registers and LDS); 0 if it cannot be queried.
+template <auto Kernel>
+int resident_slots(int threads) {
   constexpr int kMaxDev = 64;
   static int cache[kMaxDev];  // written once per device with the same value
   int dev = 0;
@@ -227,7 +229,7 @@ int resident_slots(K kernel, int threads) {
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, Kernel, threads, 0) != hipSuccess)
     return 0;
   const int slots = cus * per_cu;
   if (dev < kMaxDev) __atomic_store_n(&cache[dev], slots, __ATOMIC_RELAXED);

@@ -756,11 +756,11 @@ hipError_t launch_one(const FwdArgs& a, int BH, hipStream_t stream,
   args.bh = BH;
   const int64_t units = (int64_t)args.n_qtiles * BH * args.n_split;
   if (units > 0x7fffffff) return hipErrorInvalidValue;
-  auto kernel =
+  constexpr auto kernel =
       fwd_kernel<D, C::BN, C::NW, C::QB, C::OCC, C::NSTG, CAUSAL, DT, PERSIST, PARTIAL, SPARSE>;
   int64_t grid = units;
   if constexpr (PERSIST) {
-    const int slots = resident_slots(kernel, C::NW * 64);
+    const int slots = resident_slots<kernel>(C::NW * 64);
     if (slots <= 0) return hipErrorInvalidValue;
     grid = std::min<int64_t>(units, slots);
     args.pin = (BH % 8 == 0 && grid % 8 == 0) ? 1 : 0;

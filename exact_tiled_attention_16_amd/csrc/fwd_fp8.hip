@@ -112,14 +112,30 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   constexpr int NDC = D / 64;        // 64-wide head-dim chunks of S
   constexpr int NDB = D / 32;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NSTG * TILEB];
+  // The non-causal persistent grid (PERSIST && !CAUSAL) copies the next
+  // unit's first two K tiles into stages 0 and 1 while the current unit's O
+  // passes through LDS: O is then staged above them.
+  constexpr bool PREFETCH = PERSIST && !CAUSAL;
+  constexpr int OROWB = 2 * D + 8;  // bytes per staged O row (8 bytes of padding)
+  constexpr int OSTB = PREFETCH ? 2 * TILEB : 0;
+  constexpr int SMEM = 2 * NSTG * TILEB > OSTB + NW * 32 * OROWB ? 2 * NSTG * TILEB
+                                                                 : OSTB + NW * 32 * OROWB;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
   FA_LDS uint8_t* lds = (FA_LDS uint8_t*)smem;  // K stage s at s*TILEB, V at (NSTG+s)*TILEB
 
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int N = a.N;
 
-  // One work unit: query tile qt of head bh.
-  auto unit = [&](const int bh_in, const int qt_in) __attribute__((always_inline)) {
+  // Q8^T operand: lane holds query qrow, head-dim bytes dc*64 + 32*hl +
+  // [0, 32).  Declared outside the unit: the persistent non-causal grid loads
+  // the next unit's rows here during the current unit's epilogue.
+  i32x8_t qf[NDC];
+
+  // One work unit: query tile qt of head bh.  nxt: the next unit of this
+  // workgroup (persistent non-causal grid), else -1; pre: this unit's Q rows
+  // and first two K tiles were fetched by the previous unit's epilogue.
+  auto unit = [&](const int bh_in, const int qt_in, const int nxt, const bool pre)
+                  __attribute__((always_inline)) {
   // The unit's indices come out of runtime divisions, which the compiler
   // does on the vector ALU; taken to scalar registers here, every address
   // and tile bound derived from them stays on the scalar unit instead of
@@ -206,19 +222,20 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
     for (int i = 0; i < G; ++i) issue(V, v0 + i, lds + (NSTG + ((v0 + i) & MSK)) * TILEB, voff_dma);
   };
 
-  // Q8^T operand: lane holds query qrow, head-dim bytes dc*64 + 32*hl + [0, 32).
-  i32x8_t qf[NDC];
+  auto load_q = [&](const uint8_t* Qh, int row) {
 #pragma unroll
-  for (int dc = 0; dc < NDC; ++dc) {
-    u32x4_t lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-    if (qrow < N) {
-      const uint8_t* p = Q + (int64_t)qrow * D + dc * 64 + 32 * hl;
-      lo = ld_global16(p);
-      hi = ld_global16(p + 16);
+    for (int dc = 0; dc < NDC; ++dc) {
+      u32x4_t lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+      if (row < N) {
+        const uint8_t* p = Qh + (int64_t)row * D + dc * 64 + 32 * hl;
+        lo = ld_global16(p);
+        hi = ld_global16(p + 16);
+      }
+      qf[dc] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     }
-    qf[dc] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-  }
+  };
+  if (!pre) load_q(Q, qrow);
 
   f32x16_t oacc[NDB];
 #pragma unroll
@@ -577,9 +594,14 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   // probabilities and P V products are exactly zero.
   // The prologue pair (-1, 0) reads K(0) and K(1), copied and published
   // first.
-  issue(K, 0, lds, koff_dma);
-  issue(K, 1, lds + TILEB, koff_dma);
-  dma_sync<GROUPED ? 0 : IPW>();
+  if (!pre) {
+    issue(K, 0, lds, koff_dma);
+    issue(K, 1, lds + TILEB, koff_dma);
+  }
+  if (GROUPED || pre)
+    dma_sync<0>();
+  else
+    dma_sync<IPW>();
   using PM2 = std::integral_constant<int, -2>;
   using PM1 = std::integral_constant<int, -1>;
   using P0 = std::integral_constant<int, 0>;
@@ -642,11 +664,21 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   // block into LDS (rows padded by 8 bytes, so the 8-byte writes of one
   // half-wave hit distinct banks), then stores whole rows, 16 bytes per lane.
   // The K/V ring is free once every wave has left the loop.
-  constexpr int OROWB = 2 * D + 8;
-  static_assert(NW * 32 * OROWB <= 2 * NSTG * TILEB, "the O blocks fit in the K/V ring");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  FA_LDS uint8_t* ost = lds + wave * 32 * OROWB;
+  if constexpr (PREFETCH) {
+    // The next unit's Q rows (this unit's are dead) and its first two K
+    // tiles, into the stages below the O blocks, in flight while O leaves.
+    if (nxt >= 0) {
+      const int nbh = nxt / a.n_qtiles, nqt = nxt % a.n_qtiles;
+      const int64_t nbase = (int64_t)nbh * N * D;
+      load_q(static_cast<const uint8_t*>(a.q8) + nbase, nqt * BM + wave * 32 + l32);
+      const uint8_t* Kn = static_cast<const uint8_t*>(a.k8) + nbase;
+      issue(Kn, 0, lds, koff_dma);
+      issue(Kn, 1, lds + TILEB, koff_dma);
+    }
+  }
+  FA_LDS uint8_t* ost = lds + OSTB + wave * 32 * OROWB;
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -675,19 +707,35 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
     a.lse[(int64_t)bh * N + qrow] = m_run * kLn2 + __logf(l_tot);
   };  // unit
 
-  if constexpr (PERSIST) {
+  if constexpr (PERSIST && CAUSAL) {
     // Causal: query tile qt costs qt + 1 key tiles; rank 0 is the last one.
     lpt_units(a.n_qtiles, a.bh, a.pin != 0, [&](int bh, int rank) {
-      unit(bh, a.n_qtiles - 1 - rank);
+      unit(bh, a.n_qtiles - 1 - rank, -1, false);
       // The next unit's first copies reuse the ring.
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     });
+  } else if constexpr (PERSIST) {
+    // Non-causal, all units alike: workgroup w takes units w, w + G, ... of
+    // the (head, query tile) order under the XCD remap of the one-unit grid
+    // below (G is a multiple of 8, so each stays on the XCD it had there),
+    // and fetches each next unit's Q rows and first K tiles during the
+    // current unit's epilogue.
+    const int total = a.n_qtiles * a.bh;
+    for (int u = blockIdx.x; u < total; u += gridDim.x) {
+      const int logical = xcd_remap(u, total);
+      const int nu = u + (int)gridDim.x;
+      unit(logical / a.n_qtiles, logical % a.n_qtiles, nu < total ? xcd_remap(nu, total) : -1,
+           u != (int)blockIdx.x);
+      // The next unit's copies and O blocks reuse the ring.
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
   } else {
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     int qt = logical % a.n_qtiles;
     if (CAUSAL) qt = a.n_qtiles - 1 - qt;  // longest key ranges first
-    unit(logical / a.n_qtiles, qt);
+    unit(logical / a.n_qtiles, qt, -1, false);
   }
 }
 
@@ -700,7 +748,11 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
 template <int D, int NW, int OCC, int NSTG, bool CAUSAL>
 hipError_t launch_one(const Fp8Args& a0, int BH, hipStream_t s) {
   constexpr int BM = 32 * NW;
-  constexpr bool PERSIST = CAUSAL && D >= 128;
+  // Non-causal launches at d = 128 also run persistent, prefetching each
+  // next unit (+0.4-1.8 % in the 16-bit forward); d = 64 fits two
+  // workgroups per CU, which overlap each other's prologues already, and at
+  // d = 256 the prefetching unit spills registers.
+  constexpr bool PERSIST = CAUSAL ? D >= 128 : D == 128;
   Fp8Args a = a0;
   a.n_qtiles = (a.N + BM - 1) / BM;
   a.bh = BH;
@@ -710,8 +762,8 @@ hipError_t launch_one(const Fp8Args& a0, int BH, hipStream_t s) {
     hipLaunchKernelGGL((fwd_fp8_kernel<D, 64, NW, OCC, NSTG, CAUSAL, false>),
                        dim3((unsigned)units), dim3(NW * 64), 0, s, a, a.k_scale, a.v_scale);
   } else {
-    auto kernel = fwd_fp8_kernel<D, 64, NW, OCC, NSTG, true, true>;
-    const int slots = resident_slots(kernel, NW * 64);
+    constexpr auto kernel = fwd_fp8_kernel<D, 64, NW, OCC, NSTG, CAUSAL, true>;
+    const int slots = resident_slots<kernel>(NW * 64);
     if (slots <= 0) return hipErrorInvalidValue;
     const int64_t grid = std::min<int64_t>(units, slots);
     a.pin = (BH % 8 == 0 && grid % 8 == 0) ? 1 : 0;
