@@ -443,18 +443,39 @@ bwd_kv3_kernel(BwdArgs a) {
     }
     wait_vmcnt<0>();  // copies past the last tile must land before LDS is released
 
-    if (key < N) {
-      uint16_t* row = static_cast<uint16_t*>(ROLE == 0 ? a.dv : a.dk) + base + (int64_t)key * D;
-      const float f = ROLE == 0 ? 1.0f : a.scale;
+    // A lane holds its key's row in 8-byte pieces, so stores straight from
+    // the accumulators would scatter each instruction over 32 rows.  Once
+    // every wave is done with the ring, each writes its 32 rows into it
+    // (padded by 8 bytes, so the 8-byte writes of one half-wave hit distinct
+    // banks) and stores whole rows, 16 bytes per lane.
+    constexpr int OROWB = 2 * D + 8;
+    static_assert(NW * 32 * OROWB <= NSTG * STAGEB, "the dK / dV blocks fit in the ring");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    FA_LDS uint8_t* ost = lds + wave * 32 * OROWB;
+    const float f = ROLE == 0 ? 1.0f : a.scale;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
+    for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          u32x2_t w;
-          w[0] = E::pack2(acc[db][4 * g + 0] * f, acc[db][4 * g + 1] * f);
-          w[1] = E::pack2(acc[db][4 * g + 2] * f, acc[db][4 * g + 3] * f);
-          *reinterpret_cast<u32x2_t*>(row + db * 32 + 8 * g + 4 * hl) = w;
-        }
+      for (int g = 0; g < 4; ++g) {
+        u32x2_t w;
+        w[0] = E::pack2(acc[db][4 * g + 0] * f, acc[db][4 * g + 1] * f);
+        w[1] = E::pack2(acc[db][4 * g + 2] * f, acc[db][4 * g + 3] * f);
+        *reinterpret_cast<FA_LDS u32x2_t*>(ost + l32 * OROWB + 2 * (db * 32 + 8 * g + 4 * hl)) = w;
+      }
+    }
+    asm volatile("" ::: "memory");
+    {
+      constexpr int LPR = D / 8;     // lanes per row, 16 bytes each
+      constexpr int RPI = 64 / LPR;  // rows per store instruction
+      const int r0 = lane / LPR, cb = (lane % LPR) * 16;
+      const int key0 = k0 + kb * 32;
+      uint8_t* dst = static_cast<uint8_t*>(ROLE == 0 ? a.dv : a.dk) + 2 * (base + (int64_t)key0 * D);
+#pragma unroll
+      for (int k = 0; k < 32 / RPI; ++k) {
+        const int r = r0 + RPI * k;
+        const u32x4_t v = ld_lds16(ost + r * OROWB + cb);
+        if (key0 + r < N) *reinterpret_cast<u32x4_t*>(dst + 2 * (int64_t)r * D + cb) = v;
       }
     }
   };
