@@ -534,7 +534,11 @@ bwd_dq_kernel(BwdArgs a) {
   constexpr int NDB = D / 32;
   constexpr int NDC = D / 16;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NSTG * TILEB];
+  // dQ leaves through LDS in fp32 rows padded by 16 bytes: at d = 128 the
+  // eight waves' blocks (132 KiB) exceed the ring, which is sized up.
+  constexpr int OROWB = 4 * D + 16;
+  constexpr int SMEM = 2 * NSTG * TILEB > NW * 32 * OROWB ? 2 * NSTG * TILEB : NW * 32 * OROWB;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
   FA_LDS uint8_t* lds = (FA_LDS uint8_t*)smem;  // K stage s at s*TILEB, V at (NSTG+s)*TILEB
 
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -760,16 +764,32 @@ bwd_dq_kernel(BwdArgs a) {
   wait_vmcnt<0>();  // copies past the last tile must land before LDS is released
 
   // dQ^T register r of block db is head dim db*32 + 8*(r/4) + 4*hl + r%4 of
-  // this lane's query.
-  if (qrow < N) {
-    float* dqrow = a.dq + base + (int64_t)qrow * D;
+  // this lane's query.  Stored straight from the accumulators, each 16-byte
+  // store would scatter over 32 rows; once every wave is done with the ring,
+  // each writes its 32 rows into LDS and stores whole rows, 16 bytes per
+  // lane.
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  FA_LDS uint8_t* ost = lds + wave * 32 * OROWB;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<f32x4_t*>(dqrow + db * 32 + 8 * g + 4 * hl) =
-            f32x4_t{dqacc[db][4 * g], dqacc[db][4 * g + 1], dqacc[db][4 * g + 2], dqacc[db][4 * g + 3]} *
-            a.scale;
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<FA_LDS f32x4_t*>(ost + l32 * OROWB + 4 * (db * 32 + 8 * g + 4 * hl)) =
+          f32x4_t{dqacc[db][4 * g], dqacc[db][4 * g + 1], dqacc[db][4 * g + 2], dqacc[db][4 * g + 3]} *
+          a.scale;
+  asm volatile("" ::: "memory");
+  {
+    constexpr int LPR = D / 4;     // lanes per row, 16 bytes (four fp32) each
+    constexpr int RPI = 64 / LPR;  // rows per store instruction
+    const int r0 = lane / LPR, cb = (lane % LPR) * 16;
+    uint8_t* dst = reinterpret_cast<uint8_t*>(a.dq + base + (int64_t)qw0 * D);
+#pragma unroll
+    for (int k = 0; k < 32 / RPI; ++k) {
+      const int r = r0 + RPI * k;
+      const u32x4_t v = ld_lds16(ost + r * OROWB + cb);
+      if (qw0 + r < N) *reinterpret_cast<u32x4_t*>(dst + 4 * (int64_t)r * D + cb) = v;
+    }
   }
   };  // unit
 
