@@ -384,14 +384,16 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
   // scheduling barrier after each step keeps the vector work spread evenly
   // under the matrix work.  DS / DP / DPV select which of the three streams
   // run (the ragged end and the causal diagonal drop some for some waves);
-  // MS masks S(j+1).  S(j) is in s_cur, P(j-1) in p_prev; S(j+1) goes to
+  // MS masks S(j) before P(j).  S(j) is in s_cur, P(j-1) in p_prev; S(j+1) goes to
   // s_nxt and P(j) to p_cur.
   constexpr int NSTEP = NKB * NDC;  // == (BN / 16) * NDB
   constexpr int NPAIR = NKB * 8;    // probability pairs per lane, tile and block
-  constexpr int PF = D >= 256 ? 1 : 2;  // fragment prefetch distance in steps
+  // Fragment prefetch distance in steps: 2 (1 at d = 256, and in the masked
+  // iterations, which hold the mask's bounds as well).
+  constexpr int PF0 = D >= 256 ? 1 : 2;
   // SECOND: the second iteration of a pair (j even), else the first.
   auto fused = [&](auto ds_tag, auto ms_tag, auto dp_tag, auto dpv_tag, auto second_tag, int j,
-                   int st, const Scores& s_cur, Scores& s_nxt, Probs& p_cur, const Probs& p_prev) {
+                   int st, Scores& s_cur, Scores& s_nxt, Probs& p_cur, const Probs& p_prev) {
     constexpr bool DS = decltype(ds_tag)::value, MS = decltype(ms_tag)::value;
     constexpr bool DP = decltype(dp_tag)::value, DPV = decltype(dpv_tag)::value;
     constexpr bool SECOND = decltype(second_tag)::value;
@@ -402,6 +404,36 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
     // st = j % NSTG (a constant in the unrolled main loops).
     const FA_LDS uint8_t* ks = lds + (PAIR ? (st + 1) & 3 : snext(st)) * TILEB;
     const FA_LDS uint8_t* vs = lds + (PAIR ? (st + 3) & 3 : sprev(st)) * TILEB;  // + NSTG * TILEB in voff
+    if constexpr (DP && MS) {
+      // The mask goes on S(j) here, before its probabilities are formed:
+      // its products completed in the previous iteration, and nothing sits
+      // between the steps and the tile's end (a mask on S(j+1) after the
+      // steps waited for their products, and the compiler sank the
+      // exponentials past its branch, out of the steps).  Register r of
+      // block kb holds key t*BN + 4*hl + (kb*32 + 8*(r/4) + r%4) with t = j;
+      // it is visible iff that constant offset is below `lim`.
+      const int t = SPARSE ? tile_of(j) : j;
+      // Block-sparse: the wave's query block does not attend to this tile.
+      bool dead = false;
+      if constexpr (SPARSE && BM > kSparseBlock)
+        dead = !((lst[1 + j] >> (24 + (wave * WQ) / kSparseBlock)) & 1);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        int lim = kn - t * BN - 4 * hl;
+        if (CAUSAL) lim = min(lim, qw0 + 32 * qb + l32 + 1 + coff - t * BN - 4 * hl);
+        if (dead) lim = -BN;
+        // Tiles of the masked tail that need no mask in any lane skip it.
+        constexpr int kMaxOff = (NKB - 1) * 32 + 27;  // largest key offset of a register
+        if (wave_any(lim <= kMaxOff)) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s_cur[qb][kb][r] = -INFINITY;
+        }
+      }
+    }
+    constexpr int PF = MS ? 1 : PF0;
     v8 kfr[PF + 1], vfr[PF + 1];
     // S(j+1) runs key block by key block (kb-major) and P(j) consumes S(j)
     // in the same order, so only about half of each score set is live at once.
@@ -479,30 +511,6 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
 #if FA_FWD_INTERLEAVE
       __builtin_amdgcn_sched_barrier(0);
 #endif
-    }
-    if constexpr (DS && MS) {
-      // Register r of block kb holds key t*BN + 4*hl + (kb*32 + 8*(r/4) + r%4)
-      // with t = j+1; it is visible iff that constant offset is below `lim`.
-      const int t = SPARSE ? tile_of(j + 1) : j + 1;
-      // Block-sparse: the wave's query block does not attend to this tile.
-      bool dead = false;
-      if constexpr (SPARSE && BM > kSparseBlock)
-        dead = !((lst[2 + j] >> (24 + (wave * WQ) / kSparseBlock)) & 1);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        int lim = kn - t * BN - 4 * hl;
-        if (CAUSAL) lim = min(lim, qw0 + 32 * qb + l32 + 1 + coff - t * BN - 4 * hl);
-        if (dead) lim = -BN;
-        // Tiles of the masked tail that need no mask in any lane skip it.
-        constexpr int kMaxOff = (NKB - 1) * 32 + 27;  // largest key offset of a register
-        if (wave_any(lim <= kMaxOff)) {
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s_nxt[qb][kb][r] = -INFINITY;
-        }
-      }
     }
     if constexpr (DP) {
       float psum[QB];
