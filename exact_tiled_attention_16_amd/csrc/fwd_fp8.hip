@@ -423,7 +423,7 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
     issue(V, j + 1, lds + (NSTG + snext(st)) * TILEB, voff_dma);
   };
   auto fused = [&](auto ds_tag, auto ms_tag, auto dp_tag, auto dpv_tag, auto vb_tag, auto pos_tag,
-                   auto ph_tag, int j, int st, const Scores& s_cur, Scores& s_nxt, Probs& p_cur,
+                   auto ph_tag, int j, int st, Scores& s_cur, Scores& s_nxt, Probs& p_cur,
                    const Probs& p_prev) {
     constexpr bool DS = decltype(ds_tag)::value, MS = decltype(ms_tag)::value;
     constexpr bool DP = decltype(dp_tag)::value, DPV = decltype(dpv_tag)::value;
@@ -475,6 +475,23 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s_nxt[kb][r] = 0.f;
+    }
+    if constexpr (DP && MS) {
+      // The mask goes on S(j) before its probabilities are formed (its
+      // products completed in the previous iteration): a mask on S(j+1)
+      // after the steps waited for their products.  Register r of block kb
+      // holds key j*BN + 4*hl + (kb*32 + 8*(r/4) + r%4).
+      int lim = N - j * BN - 4 * hl;
+      if (CAUSAL) lim = min(lim, qrow + 1 - j * BN - 4 * hl);
+      // Tiles of the masked tail that need no mask in any lane skip it.
+      constexpr int kMaxOff = (NKB - 1) * 32 + 27;  // largest key offset of a register
+      if (wave_any(lim <= kMaxOff)) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s_cur[kb][r] = -INFINITY;
+      }
     }
     float ps0 = -0.f, ps1 = -0.f;
     // The P(j-1) V products come first and the S(j+1) products last, so O is
@@ -558,20 +575,6 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
     if constexpr (GROUPED) {
       ks_pre = kscale(j + 1);
       vs_pre = vscale(j + 1);
-    }
-    if constexpr (DS && MS) {
-      const int t = j + 1;
-      int lim = N - t * BN - 4 * hl;
-      if (CAUSAL) lim = min(lim, qrow + 1 - t * BN - 4 * hl);
-      // Tiles of the masked tail that need no mask in any lane skip it.
-      constexpr int kMaxOff = (NKB - 1) * 32 + 27;  // largest key offset of a register
-      if (wave_any(lim <= kMaxOff)) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s_nxt[kb][r] = -INFINITY;
-      }
     }
     if constexpr (DP) finish_tile(s_cur, p_cur, mul, ps0 + ps1, vchange, vfrom, vs_acc);
     if constexpr (!GROUPED)
