@@ -681,9 +681,9 @@ fwd_kernel(FwdArgs a, const int* __restrict__ bs_list) {
   } else if constexpr (PERSIST) {
     // Non-causal, all units alike: workgroup w takes units w, w + G, ... of
     // the (head, query tile) order under the XCD remap of the one-unit grid
-    // below (G is a multiple of 8, so each stays on the XCD it had there),
-    // and fetches each next unit's Q rows and first K tiles during the
-    // current unit's epilogue.
+    // below (when G is a multiple of 8, as the full grid of one workgroup per
+    // CU is, each unit stays on the XCD it had there), and fetches each next
+    // unit's Q rows and first K tiles during the current unit's epilogue.
     static_assert(!PARTIAL && !SPARSE && NSTG >= 3, "plain non-causal forward");
     const int total = a.n_qtiles * a.bh;
     for (int u = blockIdx.x; u < total; u += gridDim.x) {

@@ -721,9 +721,9 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   } else if constexpr (PERSIST) {
     // Non-causal, all units alike: workgroup w takes units w, w + G, ... of
     // the (head, query tile) order under the XCD remap of the one-unit grid
-    // below (G is a multiple of 8, so each stays on the XCD it had there),
-    // and fetches each next unit's Q rows and first K tiles during the
-    // current unit's epilogue.
+    // below (when G is a multiple of 8, as the full grid of one workgroup per
+    // CU is, each unit stays on the XCD it had there), and fetches each next
+    // unit's Q rows and first K tiles during the current unit's epilogue.
     const int total = a.n_qtiles * a.bh;
     for (int u = blockIdx.x; u < total; u += gridDim.x) {
       const int logical = xcd_remap(u, total);
