@@ -177,7 +177,7 @@ def build_legs(torch, fa, dev):
     # One fa_bwd call launches three kernels back to back; the leg is timed
     # (and its roofline reported) as that one launch sequence.
     legs.append(dict(name="bwd_bf16", call=bwd_call, flops=2.5 * fwd_flops(B, H, N, d),
-                     dtype="bf16", kernel="bwd_pre_kernel+bwd_kv3_kernel+bwd_dq_kernel"))
+                     dtype="bf16", kernel="bwd_dq_kernel+bwd_kv3_kernel"))
     outputs = {"fwd_bf16": (o, lse), "fwd_fp8": (o8,), "bwd_bf16": (dq, dk, dv)}
     return legs, (qd, kd, vd), outputs
 

@@ -8,9 +8,21 @@
 //     dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),
 //     dK = scale * dS^T Q,  dQ = scale * dS K.
 //
-// Kernels:
-//   bwd_pre_kernel  per query row: -LSE / scale and -D into two planes of the
-//                   workspace (all rows of one, then all rows of the other).
+// Kernels, in launch order (bwd_dq_kernel first: it also forms the row
+// statistics, which bwd_kv3_kernel reads):
+//   bwd_dq_kernel   one workgroup per (b, h, tile of 32*NW queries), built like
+//                   the forward: Q and dO rows stay in registers, K and V tiles
+//                   stream through a four-stage LDS ring (one workgroup
+//                   barrier per pair of key tiles); per key tile it
+//                   recomputes S^T = K Q^T and dP^T = V dO^T, forms dS^T and
+//                   accumulates dQ^T += K^T dS^T in registers, written once at
+//                   the end.  Recomputing two products costs 2/5 more matrix
+//                   work than accumulating dQ with atomics from the dK/dV pass,
+//                   whose fp32 atomic traffic (every key tile adds a full dQ
+//                   tile) is bound by the L2 atomic units.  At its start it
+//                   writes each of its query rows' -LSE / scale and -D into
+//                   two planes of the workspace (all rows of one, then all
+//                   rows of the other).
 //   bwd_kv3_kernel  one workgroup of 8 waves per (b, h, tile of 128 keys); the
 //                   four 32-key blocks each get two waves that share a SIMD:
 //                   one keeps the block's K rows and dV accumulator (S, P,
@@ -25,16 +37,6 @@
 //                   reads (dV, dK).  The S and dP accumulators start from the
 //                   row statistics, and dK = scale * dS^T Q is scaled once at
 //                   the end.
-//   bwd_dq_kernel   one workgroup per (b, h, tile of 32*NW queries), built like
-//                   the forward: Q and dO rows stay in registers, K and V tiles
-//                   stream through a four-stage LDS ring (one workgroup
-//                   barrier per pair of key tiles); per key tile it
-//                   recomputes S^T = K Q^T and dP^T = V dO^T, forms dS^T and
-//                   accumulates dQ^T += K^T dS^T in registers, written once at
-//                   the end.  Recomputing two products costs 2/5 more matrix
-//                   work than accumulating dQ with atomics from the dK/dV pass,
-//                   whose fp32 atomic traffic (every key tile adds a full dQ
-//                   tile) is bound by the L2 atomic units.
 //   Rows past N (queries or keys) arrive as zeros; every product they enter
 //   is then exactly zero or never stored, so only the causal mask is applied.
 #include <algorithm>
@@ -60,36 +62,6 @@ template <> __device__ __forceinline__ float to_f32<0>(uint16_t x) {
 }
 template <> __device__ __forceinline__ float to_f32<1>(uint16_t x) {
   return (float)__builtin_bit_cast(_Float16, x);
-}
-
-// Per row: stat[row] = -LSE / scale and stat[rows + row] = -sum_c dO[row][c]
-// * O[row][c], the starting values of the S and dP accumulators of the
-// backward kernels.  D/8 threads per row.
-template <int D, int DT>
-__global__ void __launch_bounds__(256)
-bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-               const float* __restrict__ lse, float* __restrict__ stat, int64_t rows,
-               float inv_scale) {
-  constexpr int TPR = D / 8;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = gid / TPR;
-  const int c = (int)(gid % TPR);
-  float acc = 0.f;
-  if (row < rows) {
-    const u32x4_t o = ld_global16(O + row * D + c * 8);
-    const u32x4_t g = ld_global16(dO + row * D + c * 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc += to_f32<DT>((uint16_t)(o[i] & 0xffff)) * to_f32<DT>((uint16_t)(g[i] & 0xffff));
-      acc += to_f32<DT>((uint16_t)(o[i] >> 16)) * to_f32<DT>((uint16_t)(g[i] >> 16));
-    }
-  }
-#pragma unroll
-  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
-  if (row < rows && c == 0) {
-    stat[row] = -lse[row] * inv_scale;
-    stat[rows + row] = -acc;
-  }
 }
 
 // Same chunk swizzle as the forward's K/V tiles (rows of 2*D bytes): both
@@ -556,8 +528,8 @@ bwd_dq_kernel(BwdArgs a) {
   const uint16_t* Kg = static_cast<const uint16_t*>(a.k) + base;
   const uint16_t* Vg = static_cast<const uint16_t*>(a.v) + base;
   const uint16_t* dOg = static_cast<const uint16_t*>(a.dout) + base;
-  const float* stat_lse = a.dsum + (int64_t)bh * N;
-  const float* stat_d = a.dsum + a.plane + (int64_t)bh * N;
+  float* stat_lse = a.dsum + (int64_t)bh * N;
+  float* stat_d = a.dsum + a.plane + (int64_t)bh * N;
 
   const int q0 = qt * BM;
   const int qw0 = q0 + wave * 32;
@@ -602,8 +574,33 @@ bwd_dq_kernel(BwdArgs a) {
     qf[dc] = __builtin_bit_cast(v8, rq);
     of[dc] = __builtin_bit_cast(v8, ro);
   }
+  // The row statistics (-LSE/scale, -D) of this lane's query, D =
+  // rowsum(dO o O): the lane holds half of the head dimension of dO already
+  // and reads the same half of O; the other half is on lane l ^ 32.  This
+  // kernel runs first and leaves them in the workspace for the dK/dV kernel.
+  float dpart = 0.f;
+  if (qrow < N) {
+    const uint16_t* Og = static_cast<const uint16_t*>(a.o) + base + (int64_t)qrow * D;
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) {
+      const u32x4_t o = ld_global16(Og + dc * 16 + 8 * hl);
+      const u32x4_t g = __builtin_bit_cast(u32x4_t, of[dc]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dpart += to_f32<DT>((uint16_t)(o[i] & 0xffff)) * to_f32<DT>((uint16_t)(g[i] & 0xffff));
+        dpart += to_f32<DT>((uint16_t)(o[i] >> 16)) * to_f32<DT>((uint16_t)(g[i] >> 16));
+      }
+    }
+  }
+  const float dsum = sum_halves(dpart);
   f32x2_t stat = {0.f, 0.f};
-  if (qrow < N) stat = f32x2_t{stat_lse[qrow], stat_d[qrow]};  // (-LSE/scale, -D)
+  if (qrow < N) {
+    stat = f32x2_t{-a.lse[(int64_t)bh * N + qrow] * a.inv_scale, -dsum};
+    if (hl == 0) {
+      stat_lse[qrow] = stat[0];
+      stat_d[qrow] = stat[1];
+    }
+  }
   const float pbias = stat[0] * c;    // -LSE * log2 e
 
   f32x16_t dqacc[NDB];
@@ -834,27 +831,20 @@ hipError_t launch_grid(BwdArgs a, int BH, bool causal, int threads, hipStream_t 
 template <int D, int NW, int BQ, int DQ_BN, int DQ_NW, int DT>
 hipError_t launch_d(const BwdArgs& a0, int BH, bool causal, hipStream_t s) {
   BwdArgs a = a0;
-  const int64_t rows = (int64_t)BH * a.N;
-  constexpr int TPR = D / 8;
-  const int64_t pre_blocks = (rows * TPR + 255) / 256;
-  if (pre_blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((bwd_pre_kernel<D, DT>), dim3((unsigned)pre_blocks), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout),
-                     a.lse, a.dsum, rows, 1.0f / a.scale);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  a.plane = rows;
+  a.plane = (int64_t)BH * a.N;
   a.bh = BH;
-  constexpr int BKV = 128;
-  a.n_ktiles = (a.N + BKV - 1) / BKV;
-  e = launch_grid<bwd_kv3_kernel<D, BQ, false, DT, false>, bwd_kv3_kernel<D, BQ, true, DT, true>>(
-      a, BH, causal, 512, s);
-  if (e != hipSuccess) return e;
+  a.inv_scale = 1.0f / a.scale;
+  // The dQ kernel first: it forms the row statistics the dK/dV kernel reads.
   constexpr int BM = 32 * DQ_NW;
   a.n_ktiles = (a.N + BM - 1) / BM;  // query tiles for the dQ kernel
-  return launch_grid<bwd_dq_kernel<D, DQ_BN, DQ_NW, false, DT, false>,
-                     bwd_dq_kernel<D, DQ_BN, DQ_NW, true, DT, true>>(a, BH, causal, DQ_NW * 64,
-                                                                      s);
+  hipError_t e = launch_grid<bwd_dq_kernel<D, DQ_BN, DQ_NW, false, DT, false>,
+                             bwd_dq_kernel<D, DQ_BN, DQ_NW, true, DT, true>>(a, BH, causal,
+                                                                             DQ_NW * 64, s);
+  if (e != hipSuccess) return e;
+  constexpr int BKV = 128;
+  a.n_ktiles = (a.N + BKV - 1) / BKV;
+  return launch_grid<bwd_kv3_kernel<D, BQ, false, DT, false>,
+                     bwd_kv3_kernel<D, BQ, true, DT, true>>(a, BH, causal, 512, s);
 }
 
 template <int DT>

@@ -81,6 +81,7 @@ struct BwdArgs {
   int pin;           // persistent schedule keeps each head on one XCD (launcher)
   float scale;
   float scale_log2;
+  float inv_scale;   // 1 / scale (launcher)
 };
 
 struct QuantArgs {
@@ -120,8 +121,8 @@ hipError_t launch_fwd_fp8(const Fp8Args& a, int B, int H, int d, bool causal, hi
 // Head dimensions the backward is built for.
 bool bwd_supported(int d);
 
-// Enqueue preprocess + main backward kernels.  Arguments are validated by the
-// caller.
+// Enqueue the backward kernels (dQ with the row statistics, then dK/dV).
+// Arguments are validated by the caller.
 hipError_t launch_bwd(const BwdArgs& a, int B, int H, int d, int dtype, bool causal,
                       hipStream_t stream);
 
