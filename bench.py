@@ -174,7 +174,7 @@ def build_legs(torch, fa, dev):
                          do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                          dv.data_ptr(), ws.data_ptr(), B, H, N, d, fa.FA_BF16, scale, 0,
                          stream)
-    # One fa_bwd call launches three kernels back to back; the leg is timed
+    # One fa_bwd call launches two kernels back to back; the leg is timed
     # (and its roofline reported) as that one launch sequence.
     legs.append(dict(name="bwd_bf16", call=bwd_call, flops=2.5 * fwd_flops(B, H, N, d),
                      dtype="bf16", kernel="bwd_dq_kernel+bwd_kv3_kernel"))
