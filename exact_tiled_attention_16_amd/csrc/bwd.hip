@@ -460,7 +460,7 @@ bwd_kv3_kernel(BwdArgs a) {
   if constexpr (PERSIST) {
     // Causal: key tile kt meets the query tiles from its diagonal on, so
     // rank 0 (the heaviest) is key tile 0.
-    lpt_units(a.n_ktiles, a.bh, a.pin != 0, [&](int bh, int rank) {
+    lpt_units(a.n_ktiles, a.bh, a.pin != 0, [&](int bh, int rank, int, int) {
       unit(bh, rank);
       // The next unit's first copies reuse the ring and the P buffers.
       __builtin_amdgcn_s_barrier();
@@ -794,7 +794,7 @@ bwd_dq_kernel(BwdArgs a) {
   if constexpr (PERSIST) {
     // Causal: query tile qt meets the key tiles up to its diagonal, so rank
     // 0 (the heaviest) is the last query tile.
-    lpt_units(a.n_ktiles, a.bh, a.pin != 0, [&](int bh, int rank) {
+    lpt_units(a.n_ktiles, a.bh, a.pin != 0, [&](int bh, int rank, int, int) {
       unit(bh, a.n_ktiles - 1 - rank);
       // The next unit's first copies reuse the ring.
       __builtin_amdgcn_s_barrier();

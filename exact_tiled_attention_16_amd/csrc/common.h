@@ -186,7 +186,9 @@ __device__ __forceinline__ void dma_sync() {
 // end with nearly the same total.  With `pin` (heads and grid both split
 // evenly over the 8 XCDs) each XCD keeps its own heads: head x + 8 i runs on
 // XCD x (workgroups w with w % 8 == x), so a head's operands stay in one L2.
-// run(head, rank) is called once per unit of this workgroup.
+// run(head, rank, next_head, next_rank) is called once per unit of this
+// workgroup, with the workgroup's following unit (-1, -1 after its last):
+// unit indices grow with the round, so the next one is the next round's.
 template <typename F>
 __device__ __forceinline__ void lpt_units(int ntiles, int nheads, bool pin, F&& run) {
   constexpr int kXcd = 8;
@@ -205,11 +207,14 @@ __device__ __forceinline__ void lpt_units(int ntiles, int nheads, bool pin, F&& 
     heads = nheads;
   }
   const int units = heads * ntiles;
+  auto unit_of = [&](int r) { return r * g + ((r & 1) ? g - 1 - v : v); };
+  auto head_of = [&](int k) { return pin ? x + kXcd * (k % heads) : k % heads; };
   for (int r = 0; r * g < units; ++r) {
-    const int k = r * g + ((r & 1) ? g - 1 - v : v);
+    const int k = unit_of(r);
     if (k < units) {
-      const int hi = k % heads;
-      run(pin ? x + kXcd * hi : hi, k / heads);
+      const int kn = unit_of(r + 1);
+      const bool more = kn < units;  // (one call site: the unit is inlined once)
+      run(head_of(k), k / heads, more ? head_of(kn) : -1, more ? kn / heads : -1);
     }
   }
 }

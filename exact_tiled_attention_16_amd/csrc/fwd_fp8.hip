@@ -112,10 +112,10 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   constexpr int NDC = D / 64;        // 64-wide head-dim chunks of S
   constexpr int NDB = D / 32;
 
-  // The non-causal persistent grid (PERSIST && !CAUSAL) copies the next
-  // unit's first two K tiles into stages 0 and 1 while the current unit's O
-  // passes through LDS: O is then staged above them.
-  constexpr bool PREFETCH = PERSIST && !CAUSAL;
+  // The persistent grids at d = 128 copy the next unit's first two K tiles
+  // into stages 0 and 1 while the current unit's O passes through LDS: O is
+  // then staged above them.
+  constexpr bool PREFETCH = PERSIST && D == 128;
   constexpr int OROWB = 2 * D + 8;  // bytes per staged O row (8 bytes of padding)
   constexpr int OSTB = PREFETCH ? 2 * TILEB : 0;
   constexpr int SMEM = 2 * NSTG * TILEB > OSTB + NW * 32 * OROWB ? 2 * NSTG * TILEB
@@ -127,13 +127,14 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
   const int N = a.N;
 
   // Q8^T operand: lane holds query qrow, head-dim bytes dc*64 + 32*hl +
-  // [0, 32).  Declared outside the unit: the persistent non-causal grid loads
-  // the next unit's rows here during the current unit's epilogue.
+  // [0, 32).  Declared outside the unit: the persistent grids load the next
+  // unit's rows here during the current unit's epilogue.
   i32x8_t qf[NDC];
 
   // One work unit: query tile qt of head bh.  nxt: the next unit of this
-  // workgroup (persistent non-causal grid), else -1; pre: this unit's Q rows
-  // and first two K tiles were fetched by the previous unit's epilogue.
+  // workgroup (persistent grids at d = 128; head * n_qtiles + query tile),
+  // else -1; pre: this unit's Q rows and first two K tiles were fetched by
+  // the previous unit's epilogue.
   auto unit = [&](const int bh_in, const int qt_in, const int nxt, const bool pre)
                   __attribute__((always_inline)) {
   // The unit's indices come out of runtime divisions, which the compiler
@@ -712,8 +713,11 @@ fwd_fp8_kernel(Fp8Args a, const float* __restrict__ k_scale, const float* __rest
 
   if constexpr (PERSIST && CAUSAL) {
     // Causal: query tile qt costs qt + 1 key tiles; rank 0 is the last one.
-    lpt_units(a.n_qtiles, a.bh, a.pin != 0, [&](int bh, int rank) {
-      unit(bh, a.n_qtiles - 1 - rank, -1, false);
+    bool pre = false;
+    lpt_units(a.n_qtiles, a.bh, a.pin != 0, [&](int bh, int rank, int nbh, int nrank) {
+      unit(bh, a.n_qtiles - 1 - rank,
+           PREFETCH && nbh >= 0 ? nbh * a.n_qtiles + a.n_qtiles - 1 - nrank : -1, pre);
+      pre = PREFETCH;
       // The next unit's first copies reuse the ring.
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
