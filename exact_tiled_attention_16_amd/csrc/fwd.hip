@@ -62,8 +62,10 @@ __device__ __forceinline__ int swz(int r) {
 // budget is sized for (1: 512 registers, 2: 256); NSTG = LDS stages per
 // tensor (2 or 3, see the pipeline description below).
 // PERSIST: the grid holds one workgroup per resident slot, and each loops
-// over the work units (b, h, query tile) of the causal heaviest-first
-// schedule (lpt_units); otherwise each workgroup takes one unit.
+// over work units (b, h, query tile): causal, those of the heaviest-first
+// schedule (lpt_units); non-causal, every G-th of the one-unit grid's order.
+// Each unit's epilogue fetches the next unit's Q rows and first K tiles.
+// Otherwise each workgroup takes one unit.
 // PARTIAL: split-KV mode.  Unit (b, h, query tile, split s) attends to keys
 // [s k_chunk, (s+1) k_chunk) only and writes O normalised over those keys in
 // fp32 and their log-sum-exp to slot s of the partial outputs; a merge kernel
