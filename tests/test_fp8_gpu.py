@@ -202,16 +202,17 @@ def test_fwd_fp8_full_size_sampled_heads(causal):
                          f"B=4 N=4096 pow2_v={pow2_v}")
 
 
-def test_fwd_fp8_persistent_grid_later_units_ragged():
-    """Non-causal d = 128 launches run one workgroup per resident slot, each
-    fetching its next unit's Q rows and first key tiles during the current
-    unit's epilogue.  B=1, H=33, N=2000 (ragged) gives 264 units of 256 rows
-    for 256 slots: heads 4, 16 and 32 hold workgroups' second units.  Whole
-    heads against the oracle on the same codes."""
-    _banner("fwd_fp8 persistent later units")
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_fp8_persistent_grid_later_units_ragged(causal):
+    """d = 128 launches run one workgroup per resident slot, each fetching
+    its next unit's Q rows and first key tiles during the current unit's
+    epilogue.  B=1, H=33, N=2000 (ragged) gives 264 units of 256 rows for
+    256 slots, so some workgroups run second units (non-causal: heads 4, 16
+    and 32 hold them).  Whole heads against the oracle on the same codes."""
+    _banner(f"fwd_fp8 persistent later units causal={causal}")
     ops = _oracle_operands(1, 33, 2000, 128, 12)
-    o, lse = _dev_fwd_fp8(ops, False)
-    _check_fp8_heads(ops, o, lse, ((0, 0), (0, 4), (0, 16), (0, 32)), False, "H=33 N=2000")
+    o, lse = _dev_fwd_fp8(ops, causal)
+    _check_fp8_heads(ops, o, lse, ((0, 0), (0, 4), (0, 16), (0, 32)), causal, "H=33 N=2000")
 
 
 @pytest.mark.parametrize("causal", [False, True])

@@ -122,20 +122,22 @@ def test_long_context_sampled(H, d):
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
-def test_persistent_grid_later_units_ragged(d):
-    """Non-causal launches run one workgroup per resident slot (256 on the
-    MI355X), each taking units w, w + G, ... and fetching the next unit's Q
-    rows and first key tiles during the current unit's epilogue.  B=1, H=33,
-    N=2000 (ragged) gives 264 units of 256 rows at d <= 128 and 528 of 128
-    rows at d = 256, so some workgroups run second (and third) units; heads
-    4, 16 and 32 hold such units at d = 128.  Whole heads against the
-    oracle."""
-    _banner(f"persistent later units d={d}")
+@pytest.mark.parametrize("causal", [False, True])
+def test_persistent_grid_later_units_ragged(d, causal):
+    """Launches run one workgroup per resident slot (256 on the MI355X), each
+    taking several units (non-causal: w, w + G, ...; causal: the
+    heaviest-first order) and fetching the next unit's Q rows and first key
+    tiles during the current unit's epilogue.  B=1, H=33, N=2000 (ragged)
+    gives 264 units of 256 rows at d <= 128 and 528 of 128 rows at d = 256,
+    so some workgroups run second (and third) units; heads 4, 16 and 32 hold
+    such units at d = 128 non-causal.  Whole heads against the oracle."""
+    _banner(f"persistent later units d={d} causal={causal}")
     B, H, N = 1, 33, 2000
     (qt, kt, vt), (q64, k64, v64) = _case(B, H, N, d, 11, "bf16")
-    o, lse = _run(qt, kt, vt, False)
+    o, lse = _run(qt, kt, vt, causal)
     for h in (0, 4, 16, 32):
-        o_ref, lse_ref = attention_fwd(q64[:, h:h + 1], k64[:, h:h + 1], v64[:, h:h + 1])
+        o_ref, lse_ref = attention_fwd(q64[:, h:h + 1], k64[:, h:h + 1], v64[:, h:h + 1],
+                                       causal=causal)
         assert max_abs(o[:, h:h + 1], o_ref) <= O_MAX_ABS, h
         assert rmse(o[:, h:h + 1], o_ref) <= O_RMSE, h
         assert max_abs(lse[:, h:h + 1], lse_ref) <= LSE_MAX_ABS, h
