@@ -102,6 +102,15 @@ def test_full_size_backward_heads(causal):
         _check(got, inp, f"head ({b},{h})", causal, sl=(slice(b, b + 1), slice(h, h + 1)))
 
 
+def test_bench_shape_backward_head():
+    """B=2, H=16, N=8192, d=128 non-causal (the shape the benchmark times):
+    one whole head against the oracle."""
+    _banner("bench shape B=2 N=8192")
+    B, H, N, d = 2, 16, 8192, 128
+    got, inp = _grads(B, H, N, d, 2, False)
+    _check(got, inp, "head (1,14)", False, sl=(slice(1, 2), slice(14, 15)))
+
+
 def test_gradient_identities_on_device_output():
     """sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i hold for the device result."""
     _banner("identities")
